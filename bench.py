@@ -1,0 +1,188 @@
+"""Benchmark of the chunkwise gated delta rule forward pass on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload main] [--no-cpu-baseline]
+
+A step is one gdn_chunk_fwd call (the whole hot path: decay prefix, Gram and
+scores, triangular solve, pseudo-values, output and state scan, all in one
+kernel) over the workload's seeded synthetic inputs, already resident in HBM.
+Prints one JSON line.  ``value`` is tokens/s = B * T / seconds per step.
+
+roofline: the fused kernel's algorithmic bytes (read q, k, v, alpha, beta,
+S0 once; write O and S_final once) divided by its mean duration, measured with
+HIP events on the stream it is launched on, against 8 TB/s HBM.
+cpu_baseline: the fp64 CPU oracle timed on this host on a bounded sample of
+the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0      # dense bf16 MFMA
+METRIC = "tokens/s and achieved TFLOP/s (% roofline), GDN fwd H=16 T=4096 d=128, 1 MI355X"
+KERNEL_SOURCES = ["gated_delta_rule_13_amd/csrc/gdn_kernels.h",
+                  "gated_delta_rule_13_amd/csrc/gdn_device.h",
+                  "gated_delta_rule_13_amd/csrc/gdn_api.hip"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gdn_fwd_main.json")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they
+    were taken on the current kernel sources; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("workload") != workload or rec.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(x, w, max_seconds_hint=20.0):
+    import numpy as np
+    import oracle
+
+    ncores = len(os.sched_getaffinity(0))
+    heads_total = w.B * w.H
+    # sample whole sequences; about 10-30 s of CPU work (8 d_k d_v fp64 flops per head-token)
+    per_head_flops = 8.0 * w.dk * w.dv * w.T
+    budget_flops = 2.0e9 * max_seconds_hint * 0.5   # ~1 GFLOP/s per thread, conservative
+    nsel = int(max(1, min(heads_total, budget_flops // per_head_flops)))
+    nsel = max(1, min(nsel, heads_total))
+    idx = np.linspace(0, heads_total - 1, nsel).round().astype(int)
+    pairs = [(int(i) // w.H, int(i) % w.H) for i in idx]
+    pick = lambda t: None if t is None else np.stack([t[b, h].double().numpy() for b, h in pairs])[None]
+    args = [pick(x["q"]), pick(x["k"]), pick(x["v"]), pick(x["alpha"]), pick(x["beta"])]
+    s0 = pick(x["S0"])
+    nthreads = min(ncores, nsel)
+    t0 = time.perf_counter()
+    oracle.recurrent(*args, S0=s0, nthreads=nthreads)
+    dt = time.perf_counter() - t0
+    head_tokens = nsel * w.T
+    # tokens/s on the metric's scale: B*T positions of all H heads per step
+    tok_s = head_tokens / dt / w.H
+    return {"value": tok_s, "unit": "tokens/s", "cores": nthreads, "kind": "oracle",
+            "sample": f"{nsel} of {heads_total} (b,h) sequences, full T={w.T}, fp64 recurrence",
+            "seconds": dt}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="main")
+    ap.add_argument("--o-dtype", default="f32", choices=["f32", "bf16"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain device copy of known size (for counter scaling)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build runs on one GPU only (every (b,h) sequence is independent; "
+              "multi-GPU sharding is described in DESIGN.md but not built)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import gated_delta_rule_13_amd as gdn
+    from gated_delta_rule_13_amd.workloads import (WORKLOADS, algorithmic_bytes,
+                                                   algorithmic_flops, make_inputs)
+
+    w = WORKLOADS[args.workload]
+    x = make_inputs(w, seed=0)
+    dev = torch.device("cuda:0")
+    d = {k: (None if x[k] is None else x[k].to(dev)) for k in ("q", "k", "v", "alpha", "beta", "S0")}
+    o_dtype = torch.float32 if args.o_dtype == "f32" else torch.bfloat16
+    O = torch.empty((w.B, w.H, w.T, w.dv), dtype=o_dtype, device=dev)
+    S = torch.empty((w.B, w.H, w.dv, w.dk), dtype=torch.float32, device=dev)
+
+    if args.copy_calibration:
+        src = torch.empty(256 * 1024 * 1024, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+
+    def step():
+        gdn.gdn_chunk_fwd(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["S0"],
+                          chunk_size=w.chunk, o_dtype=o_dtype, O=O, S_final=S)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream(dev)
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        starts[i].record(stream)
+        step()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kern_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    kern_ms.sort()
+    mean_kern_s = sum(kern_ms) / len(kern_ms) / 1e3
+    ms_per_step = wall / args.steps * 1e3
+
+    o_bytes = 4 if o_dtype == torch.float32 else 2
+    alg_bytes = algorithmic_bytes(w, o_bytes=o_bytes)
+    alg_flops = algorithmic_flops(w)
+    tokens = w.B * w.T
+    value = tokens / (wall / args.steps)
+    achieved_gbs = alg_bytes / mean_kern_s / 1e9
+    traffic = measured_traffic(w.name) if args.o_dtype == "f32" else None
+
+    rec = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "T": w.T, "d_k": w.dk, "d_v": w.dv,
+                   "chunk": w.chunk, "o_dtype": args.o_dtype, "parallelism": "none (1 GPU)"},
+        "head_tokens_per_s": tokens * w.H / (wall / args.steps),
+        "tflops": alg_flops / (wall / args.steps) / 1e12,
+        "kernel_ms": {"mean": mean_kern_s * 1e3, "p10": kern_ms[len(kern_ms) // 10],
+                      "p50": kern_ms[len(kern_ms) // 2], "p90": kern_ms[(9 * len(kern_ms)) // 10]},
+        "roofline": {"bound": "hbm", "achieved": achieved_gbs, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": achieved_gbs / HBM_PEAK_GBS, "traffic": traffic,
+                     "algorithmic_bytes": alg_bytes,
+                     "mfma_frac": alg_flops / mean_kern_s / 1e12 / BF16_PEAK_TFLOPS},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(x, w)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

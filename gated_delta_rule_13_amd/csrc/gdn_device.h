@@ -1,0 +1,76 @@
+// gdn_device.h -- gfx950 building blocks for the chunkwise gated delta rule:
+// MFMA fragment helpers, bf16 hi/lo splitting, wave-level scans.
+//
+// MFMA shapes used (CDNA4, wave64):
+//   v_mfma_f32_16x16x32_bf16  A 16x32, B 32x16, D 16x16 fp32
+//   v_mfma_f32_16x16x4_f32    A 16x4,  B 4x16,  D 16x16 fp32
+// Lane layout, with lane = 16*h + n (n in 0..15, h in 0..3):
+//   A operand: row m = n, k-slots h*KPL .. h*KPL+KPL-1  (KPL = 8 bf16 / 1 f32)
+//   B operand: col  = n, same k-slots
+//   D (4 floats): col = n, rows 4*h + j, j = 0..3
+// The contraction index may be permuted freely as long as A and B agree; the
+// kernels use that to feed an accumulator (rows 4h+j of consecutive tiles)
+// straight back as the next product's operand, and load the other operand
+// from LDS with the same permutation ("perm-k").
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gdn {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+
+__device__ __forceinline__ f32x4 mfma_bf16(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma_f32(float a, float b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+
+// Round to bf16 (nearest-even) and the exact fp32 residual rounded again:
+// x ~= hi + lo with |x - hi - lo| <= 2^-17 |x| (about 16 significant bits).
+__device__ __forceinline__ void split_bf16(float x, __bf16& hi, __bf16& lo) {
+    hi = (__bf16)x;
+    lo = (__bf16)(x - (float)hi);
+}
+
+// Eight accumulator values (two consecutive 16-row tiles, rows 4h+j) as the
+// hi / lo halves of a perm-k bf16 operand.
+__device__ __forceinline__ void split8(const f32x4& a0, const f32x4& a1, bf16x8& hi, bf16x8& lo) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        __bf16 h0, l0, h1, l1;
+        split_bf16(a0[e], h0, l0);
+        split_bf16(a1[e], h1, l1);
+        hi[e] = h0; lo[e] = l0;
+        hi[e + 4] = h1; lo[e + 4] = l1;
+    }
+}
+
+// perm-k bf16 operand from an LDS row: elements [32s + 4h, +4) and
+// [32s + 16 + 4h, +4) -- matches split8 of accumulator tiles 2s, 2s+1.
+__device__ __forceinline__ bf16x8 ld_perm8(const __bf16* row, int s, int h) {
+    const bf16x4 a = *reinterpret_cast<const bf16x4*>(row + 32 * s + 4 * h);
+    const bf16x4 b = *reinterpret_cast<const bf16x4*>(row + 32 * s + 16 + 4 * h);
+    return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+// natural bf16 operand from an LDS row: elements [32s + 8h, +8).
+__device__ __forceinline__ bf16x8 ld_nat8(const __bf16* row, int s, int h) {
+    return *reinterpret_cast<const bf16x8*>(row + 32 * s + 8 * h);
+}
+
+// Inclusive prefix sum over the first n lanes of a wave (n <= 64).
+__device__ __forceinline__ float wave_inclusive_scan(float x, int lane) {
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        float y = __shfl_up(x, off, 64);
+        if (lane >= off) x += y;
+    }
+    return x;
+}
+
+}  // namespace gdn

@@ -1,0 +1,136 @@
+/*
+ * gdn.h -- C ABI of the MI355X (gfx950) chunkwise-parallel gated delta rule.
+ *
+ * The operation (all pages agree once the orientation is fixed; S is
+ * d_v x d_k and o = S q):
+ *
+ *     S_t = alpha_t S_{t-1} (I - beta_t k_t k_t^T) + beta_t v_t k_t^T
+ *     o_t = S_t q_t                     (the output sees token t's write)
+ *
+ * Sources: "从零开始的 GDN 推导", the recurrent form under the notation
+ * section (gate alpha_t multiplying the erased state) and the section on O
+ * (o_t = q_t S_{t+1}, i.e. inclusive); "RNN的复兴03:现代RNN的并行计算",
+ * section 1, equation (2) (S in R^{d_v x d_k}); the circuit-complexity page,
+ * "类 RNN 模型训练" (o_t = S_t q_t).  The library evaluates it with the
+ * chunkwise-parallel method of "从零开始的 GDN 推导" (UT transform, W and U,
+ * per-chunk state and output, chunks chained), which reaches the same result
+ * up to rounding order.
+ *
+ * Conventions for every entry point:
+ *  - Tensor pointers are DEVICE pointers to row-major, contiguous memory on
+ *    the current HIP device; the caller owns all of them.  The library never
+ *    allocates, frees or keeps a pointer after the call returns.
+ *  - Calls are stream-ordered and asynchronous: `stream` is a hipStream_t
+ *    (NULL = the default stream).  The return value reports argument
+ *    validation and launch errors; a fault inside a kernel surfaces at the
+ *    caller's next synchronisation.
+ *  - No global mutable state: the functions are thread-safe and re-entrant.
+ *  - Values are not checked: NaN or Inf in the inputs propagate to the
+ *    outputs of the affected (b, h) sequence only.
+ *  - Nothing is written when validation fails.
+ */
+#ifndef GDN_H
+#define GDN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    GDN_OK = 0,
+    GDN_ERR_NULL_ARG = 1,     /* a required pointer is NULL                   */
+    GDN_ERR_BAD_SHAPE = 2,    /* B, H, T < 1, or a dimension out of range     */
+    GDN_ERR_BAD_DTYPE = 3,    /* dtype code not one of gdn_dtype              */
+    GDN_ERR_UNSUPPORTED = 4,  /* valid but not built: e.g. chunk/d_k/dtype mix */
+    GDN_ERR_WORKSPACE = 5,    /* workspace smaller than the query returned    */
+    GDN_ERR_HIP = 6           /* the HIP runtime reported an error            */
+} gdn_status;
+
+typedef enum { GDN_BF16 = 0, GDN_F32 = 1 } gdn_dtype;
+
+typedef struct {
+    int32_t B, H, T;          /* batch, heads, sequence length (T >= 1)        */
+    int32_t d_k, d_v;         /* key/query and value head dimensions           */
+    int32_t chunk_size;       /* C: tokens per chunk                           */
+    int32_t qkv_dtype;        /* gdn_dtype of q, k and v (one dtype for all)   */
+    int32_t o_dtype;          /* gdn_dtype of O (GDN_F32 recommended)          */
+} gdn_shape;
+
+/*
+ * Supported combinations (anything else that is well-formed returns
+ * GDN_ERR_UNSUPPORTED):
+ *   qkv_dtype GDN_BF16: chunk_size in {32, 64}, d_k in {32, 64, 128},
+ *                       d_v a multiple of 16 in [16, 1024];
+ *   qkv_dtype GDN_F32:  chunk_size in {16, 32, 64}, d_k in {16, 32, 64},
+ *                       d_v a multiple of 16 in [16, 1024].
+ * T may be any value >= 1; a last chunk shorter than chunk_size is handled
+ * exactly (padding tokens are identity transitions).
+ */
+
+/*
+ * Bytes of device workspace gdn_chunk_fwd needs for this shape (0 for the
+ * fused kernels of this version).  Returns (size_t)-1 if the shape is
+ * invalid or unsupported.
+ */
+size_t gdn_chunk_fwd_workspace_bytes(const gdn_shape* s);
+
+/*
+ * Chunkwise-parallel forward pass.  Layouts:
+ *   q, k     [B, H, T, d_k]   qkv_dtype   (k rows are usually L2-normalised
+ *                                          by the caller; not required)
+ *   v        [B, H, T, d_v]   qkv_dtype
+ *   alpha    [B, H, T] float, gate in (0, 1]; NULL means alpha = 1 (no gate).
+ *            alpha <= 0 is outside the method (its logarithm is used).
+ *   beta     [B, H, T] float, any finite value (the pages use (0, 2)).
+ *   S0       [B, H, d_v, d_k] float initial state; NULL means zero.
+ *   O        [B, H, T, d_v]   o_dtype, written.
+ *   S_final  [B, H, d_v, d_k] float, written; may be the same pointer as S0
+ *            (the state is updated in place).
+ * workspace / workspace_bytes: at least gdn_chunk_fwd_workspace_bytes(s)
+ * bytes of device memory (may be NULL when that is 0).
+ */
+gdn_status gdn_chunk_fwd(const gdn_shape* s,
+                         const void* q, const void* k, const void* v,
+                         const float* alpha, const float* beta, const float* S0,
+                         void* O, float* S_final,
+                         void* workspace, size_t workspace_bytes,
+                         void* stream);
+
+/*
+ * Chunk-local quantities of the same method, for inspection and testing of
+ * the intermediate stages.  For every chunk c (NT = ceil(T / C) chunks, the
+ * last one zero-padded to C tokens):
+ *   T_out  [B, H, NT, C, C] float: T = (I - A)^{-1}, A strictly lower with
+ *          A_ri = -beta_r exp(g_r - g_i) k_r.k_i (i < r), g the chunk-local
+ *          inclusive cumulative sum of log alpha ("从零开始的 GDN 推导",
+ *          UT transform, with L = -A);
+ *   W_out  [B, H, T, d_k] float: W = T diag(beta) diag(exp(g)) K;
+ *   U_out  [B, H, T, d_v] float: U = T diag(beta) V ("S 的推导").
+ * Any of the three output pointers may be NULL (that output is skipped).
+ * Same support matrix and conventions as gdn_chunk_fwd.
+ */
+gdn_status gdn_chunk_prep(const gdn_shape* s,
+                          const void* k, const void* v,
+                          const float* alpha, const float* beta,
+                          float* T_out, float* W_out, float* U_out,
+                          void* workspace, size_t workspace_bytes,
+                          void* stream);
+
+/* Static text for a status code. */
+const char* gdn_status_string(gdn_status st);
+
+/* Text of the last error on the calling thread (HIP error string or the
+ * reason a shape was rejected); "" if none.  Valid until the next call. */
+const char* gdn_last_error(void);
+
+/* Library version: major * 10000 + minor * 100 + patch. */
+int32_t gdn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_H */

@@ -1,0 +1,119 @@
+"""C ABI of libgdn.so on the CPU: it loads, exports every function that
+include/gdn.h declares, and rejects bad arguments before any launch.  No
+compute call is made (every call here fails validation)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import gated_delta_rule_13_amd as gdn
+from gated_delta_rule_13_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gdn.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        from gated_delta_rule_13_amd.build import build
+        build()
+    return _lib.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gdn_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_what_binding_expects():
+    assert declared_functions() == sorted(_lib.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH],
+                         capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (gdn_[a-z_0-9]+)$", out, flags=re.M))
+    for name in declared_functions():
+        assert name in exported, name
+        assert hasattr(lib, name)
+
+
+def shape(**kw):
+    base = dict(B=1, H=2, T=100, d_k=128, d_v=128, chunk_size=64, qkv_dtype=0, o_dtype=1)
+    base.update(kw)
+    return _lib.GdnShape(**base)
+
+
+FAKE = ctypes.c_void_p(0x10000)   # never dereferenced: validation fails first
+
+
+def fwd(lib, s, **ptrs):
+    p = dict(q=FAKE, k=FAKE, v=FAKE, alpha=None, beta=FAKE, S0=None, O=FAKE, S=FAKE)
+    p.update(ptrs)
+    sp = ctypes.byref(s) if s is not None else None
+    return lib.gdn_chunk_fwd(sp, p["q"], p["k"], p["v"], p["alpha"], p["beta"], p["S0"],
+                             p["O"], p["S"], None, 0, None)
+
+
+@pytest.mark.parametrize("kw,expected", [
+    (dict(B=0), 2), (dict(H=-1), 2), (dict(T=0), 2), (dict(d_k=0), 2),
+    (dict(qkv_dtype=7), 3), (dict(o_dtype=-1), 3),
+    (dict(chunk_size=48), 4), (dict(chunk_size=16), 4), (dict(d_k=256), 4),
+    (dict(d_v=40), 4), (dict(d_v=2048), 4), (dict(qkv_dtype=1, d_k=128), 4),
+])
+def test_bad_shapes_rejected(lib, kw, expected):
+    # a mismatched q pointer (odd address) could never reach a launch either
+    assert fwd(lib, shape(**kw), q=ctypes.c_void_p(0x10001)) == expected
+    assert lib.gdn_last_error().decode() != ""
+    assert lib.gdn_chunk_fwd_workspace_bytes(ctypes.byref(shape(**kw))) == ctypes.c_size_t(-1).value
+
+
+def test_null_arguments_rejected(lib):
+    assert fwd(lib, None) == 1
+    for name in ("q", "k", "v", "beta", "O", "S"):
+        assert fwd(lib, shape(), **{name: None}) == 1, name
+
+
+def test_misaligned_pointers_rejected(lib):
+    for name in ("q", "k", "v", "beta", "O", "S", "alpha", "S0"):
+        assert fwd(lib, shape(), **{name: ctypes.c_void_p(0x10004)}) == 4, name
+
+
+def test_prep_validation(lib):
+    s = shape()
+    assert lib.gdn_chunk_prep(None, FAKE, FAKE, None, FAKE, None, None, None, None, 0, None) == 1
+    assert lib.gdn_chunk_prep(ctypes.byref(shape(B=0)), FAKE, FAKE, None, FAKE, FAKE, None, None,
+                              None, 0, None) == 2
+    assert lib.gdn_chunk_prep(ctypes.byref(s), None, FAKE, None, FAKE, FAKE, None, None,
+                              None, 0, None) == 1
+    # nothing requested: no launch, OK
+    assert lib.gdn_chunk_prep(ctypes.byref(s), FAKE, FAKE, None, FAKE, None, None, None,
+                              None, 0, None) == 0
+
+
+def test_workspace_query_and_strings(lib):
+    for kw in (dict(), dict(qkv_dtype=1, d_k=16, d_v=16, chunk_size=16),
+               dict(chunk_size=32), dict(d_v=256)):
+        assert lib.gdn_chunk_fwd_workspace_bytes(ctypes.byref(shape(**kw))) == 0
+    for code in range(7):
+        assert lib.gdn_status_string(code).decode()
+    assert lib.gdn_version() >= 100
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(_lib, "_lib", None)
+    with pytest.raises(RuntimeError, match="missing"):
+        _lib.load()
+
+
+def test_binding_rejects_cpu_tensors():
+    import torch
+    x = torch.zeros(1, 1, 4, 16)
+    b = torch.zeros(1, 1, 4)
+    with pytest.raises(ValueError, match="GPU"):
+        gdn.gdn_chunk_fwd(x, x, x, None, b)
