@@ -8,6 +8,7 @@
 
 #include "gdn.h"
 #include "gdn_kernels.h"
+#include "gdn_pipe.h"
 
 namespace {
 
@@ -92,6 +93,40 @@ void launch_prep(const gdn::FwdParams& p, long nblocks, hipStream_t st) {
 
 using Launcher = void (*)(const gdn::FwdParams&, long, hipStream_t);
 
+template <int C, int DK, int NS>
+void launch_pipe(const gdn::FwdParams& p, long nblocks, hipStream_t st) {
+    hipLaunchKernelGGL((gdn::gdn_fwd_pipe_kernel<C, DK, NS>), dim3((unsigned)nblocks),
+                       dim3((NS + gdn::kPrepWaves) * 64), 0, st, p);
+}
+
+// Pipelined kernel: bf16 inputs, C in {32, 64}, d_k in {64, 128}.  NS scan
+// waves of 16 value columns each per workgroup: the largest of 4, 2, 1 that
+// divides d_v / 16 and still gives one workgroup per compute unit (256).
+bool pipe_supported(const gdn_shape& s) {
+    return s.qkv_dtype == GDN_BF16 && (s.chunk_size == 32 || s.chunk_size == 64) &&
+           (s.d_k == 64 || s.d_k == 128);
+}
+int choose_scan_waves(const gdn_shape& s) {
+    const long heads = (long)s.B * s.H;
+    const int cols16 = s.d_v / 16;
+    for (int ns : {4, 2})
+        if (cols16 % ns == 0 && heads * (cols16 / ns) >= 256) return ns;
+    return 1;
+}
+Launcher pick_pipe(const gdn_shape& s, int ns) {
+    const int C = s.chunk_size, DK = s.d_k;
+#define GDN_PIPE(CC, KK)                                                        \
+    if (C == CC && DK == KK)                                                    \
+        return ns == 4 ? launch_pipe<CC, KK, 4>                                 \
+                       : ns == 2 ? launch_pipe<CC, KK, 2> : launch_pipe<CC, KK, 1>;
+    GDN_PIPE(64, 128)
+    GDN_PIPE(64, 64)
+    GDN_PIPE(32, 128)
+    GDN_PIPE(32, 64)
+#undef GDN_PIPE
+    return nullptr;
+}
+
 template <int C, int DK, bool BF>
 Launcher pick_nw(int nw, bool prep) {
     switch (nw) {
@@ -152,8 +187,9 @@ gdn_status gdn_chunk_fwd(const gdn_shape* s, const void* q, const void* k, const
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(O) || !aligned16(S_final) ||
         (S0 && !aligned16(S0)) || !aligned16(beta) || (alpha && !aligned16(alpha)))
         return fail(GDN_ERR_UNSUPPORTED, "tensor pointers must be 16-byte aligned");
-    const int nw = choose_waves(*s);
-    const Launcher launch = pick(*s, nw, false);
+    const bool piped = pipe_supported(*s);
+    const int nw = piped ? choose_scan_waves(*s) : choose_waves(*s);
+    const Launcher launch = piped ? pick_pipe(*s, nw) : pick(*s, nw, false);
     if (!launch) return fail(GDN_ERR_UNSUPPORTED, "shape not built");
     gdn::FwdParams p{};
     p.q = q;

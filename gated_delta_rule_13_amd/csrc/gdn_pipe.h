@@ -1,0 +1,542 @@
+// gdn_pipe.h -- software-pipelined fused kernel (bf16 inputs) for the
+// chunkwise gated delta rule on gfx950.
+//
+// Same chunk algebra as gdn_kernels.h ("从零开始的 GDN 推导": A, U and W, S
+// update, O update; transposed to the d_v x d_k state).  Two changes of
+// evaluation order, both exact in real arithmetic:
+//
+// 1. T = (I - A)^{-1} is never formed.  The pseudo-values solve the unit
+//    lower-triangular system (I - A) V' = diag(beta) Y with
+//    Y = V - diag(exp g) K S^T (so that V' = U - W S^T), by forward
+//    substitution over 16-row blocks ("RNN的复兴03", section 2.3.1, grouped
+//    by blocks):
+//        V'_b = T_bb (diag(beta_b) Y_b + sum_{c<b} A_bc V'_c),
+//    where T_bb = (I - A_bb)^{-1} are the 16 x 16 diagonal blocks, solved by
+//    forward substitution on VALU (one lane per column).  The coupling terms
+//    A_bc V'_c are dense 16 x 16 x 16 contractions and run on MFMA.
+// 2. Work is split by role inside the workgroup: NS "scan" waves each own 16
+//    value columns and that slice of the fp32 state (S^T in MFMA
+//    accumulators); NP = 4 "prep" waves build the next chunk's chunk-local
+//    quantities (decay prefix, Gram matrix, masked scores, diagonal-block
+//    solves) while the scan waves consume the current chunk.  Per chunk:
+//       phase A: scan  X = K S^T, Z^T = S Q^T
+//                prep  form A / P / T_bb of this chunk, stage the next one
+//       phase B: scan  block substitution for V', O^T = Z^T + V'^T P^T,
+//                      state update
+//                prep  Gram matrix and scores of the next chunk (MFMA)
+//    Keys, queries and transposed keys are double-buffered in LDS.  The
+//    output products are taken transposed (operands swapped) so that each
+//    lane ends with four consecutive columns of one output row.
+//
+// Precision: as in gdn_kernels.h -- inputs exact in bf16, every derived MFMA
+// operand split into bf16 hi + lo, fp32 accumulation and fp32 state.
+#pragma once
+#include <type_traits>
+
+#include "gdn_device.h"
+#include "gdn_kernels.h"
+
+namespace gdn {
+
+typedef __attribute__((ext_vector_type(4))) short s16x4;
+
+__device__ __forceinline__ f32x4 mfma16_bf16(bf16x4 a, bf16x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a),
+                                                     __builtin_bit_cast(s16x4, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ void split4(f32x4 x, bf16x4& hi, bf16x4& lo) {
+    hi = __builtin_convertvector(x, bf16x4);
+    const f32x4 back = __builtin_convertvector(hi, f32x4);
+    lo = __builtin_convertvector(x - back, bf16x4);
+}
+
+// Order LDS traffic of this wave (cross-lane exchange through LDS).
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0)
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+    if constexpr (I < N) {
+        f(std::integral_constant<int, I>{});
+        static_for<I + 1, N>(f);
+    }
+}
+
+constexpr int kPrepWaves = 4;
+
+template <int C, int DK>
+struct alignas(16) PipeLds {
+    static constexpr int NT = C / 16;
+    static constexpr int KP = DK + 8;   // row stride of key / query tiles (bf16)
+    static constexpr int CP = C + 8;    // row stride of C-wide rows (bf16)
+    __bf16 K[2][C][KP];
+    __bf16 Q[2][C][KP];
+    __bf16 Kt[2][DK][CP];
+    __bf16 Ph[C][CP];                   // masked decayed scores, hi
+    __bf16 Pl[C][CP];                   //                        lo
+    __bf16 Bh[NT][NT][16][24];          // [b][c<b]: A_bc, [b][b]: T_bb (hi)
+    __bf16 Bl[NT][NT][16][24];          //                               (lo)
+    float Add[NT][16][20];              // diagonal blocks of A, fp32 (16-byte rows)
+    float g2[2][C];                     // inclusive cumsum of log2 alpha
+    float eg[2][C];                     // 2^g2 = exp(g)
+    float dec[2][C];                    // exp(g_last - g)
+    float beta[2][C];
+    float glast[2];                     // exp(g_last)
+};
+
+// Chunk-local tile jobs of the prep waves.  Kinds: 0 = diagonal block of A
+// (kept fp32 for the diagonal solve), 1 = off-diagonal block of A, 2 = block
+// of the masked scores P.  Prep wave w < NT takes diagonal block w (and then
+// solves it); the other blocks go round-robin.  Encoding:
+// (kind << 16) | (rt << 8) | ct for tile (rt, ct), ct <= rt.
+template <int NT, int NP>
+struct PrepJobs {
+    static constexpr int NPAIR = NT * (NT + 1) / 2;
+    static constexpr int NOFF = NT * (NT - 1) / 2;
+    static constexpr int NREST = NOFF + NPAIR;
+    static constexpr int pair_rt(int p) {
+        int rt = 0, ct = p;
+        while (ct > rt) { ct -= rt + 1; ++rt; }
+        return rt;
+    }
+    static constexpr int pair_ct(int p) {
+        int rt = 0, ct = p;
+        while (ct > rt) { ct -= rt + 1; ++rt; }
+        return ct;
+    }
+    static constexpr int off_pair(int j) {
+        int cnt = 0;
+        for (int q = 0; q < NPAIR; ++q)
+            if (pair_rt(q) != pair_ct(q)) {
+                if (cnt == j) return q;
+                ++cnt;
+            }
+        return 0;
+    }
+    // k-th job of the round-robin list (off-diagonal A blocks, then P blocks)
+    static constexpr int rest(int k) {
+        if (k < NOFF) {
+            const int q = off_pair(k);
+            return (1 << 16) | (pair_rt(q) << 8) | pair_ct(q);
+        }
+        const int q = k - NOFF;
+        return (2 << 16) | (pair_rt(q) << 8) | pair_ct(q);
+    }
+    static constexpr int owner(int k) { return (NT + k) % NP; }
+    static constexpr int count(int w) {
+        int n = w < NT ? 1 : 0;
+        for (int k = 0; k < NREST; ++k) n += owner(k) == w;
+        return n;
+    }
+    static constexpr int job(int w, int j) {
+        if (w < NT) {
+            if (j == 0) return (w << 8) | w;
+            --j;
+        }
+        for (int k = 0; k < NREST; ++k)
+            if (owner(k) == w) {
+                if (j == 0) return rest(k);
+                --j;
+            }
+        return -1;
+    }
+    static constexpr int maxjobs() {
+        int m = 0;
+        for (int w = 0; w < NP; ++w) m = count(w) > m ? count(w) : m;
+        return m;
+    }
+};
+
+template <int C, int DK, int NS>
+__global__ __launch_bounds__((NS + kPrepWaves) * 64) void gdn_fwd_pipe_kernel(FwdParams p) {
+    constexpr int NP = kPrepWaves;
+    using L = PipeLds<C, DK>;
+    using J = PrepJobs<C / 16, NP>;
+    constexpr int NT = C / 16;
+    constexpr int NK = DK / 16;
+    constexpr int DVT = 16 * NS;
+    constexpr int NTHR = (NS + NP) * 64;
+    constexpr int KV = C * DK / 8;        // 16-byte vectors in a key tile
+    constexpr int NKV = KV / (64 * NP);   // per prep lane
+    constexpr int MAXJ = J::maxjobs();
+    static_assert(KV % (64 * NP) == 0, "key tile must split over the prep waves");
+    static_assert(sizeof(L) <= 160 * 1024, "LDS budget");
+    __shared__ L s;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    // wave index as a scalar: role branches below are uniform per wave
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int n = lane & 15;
+    const int h = lane >> 4;
+    const bool scan = wave < NS;
+    const int pw = wave - NS;             // prep wave 0..NP-1
+    const int plane = tid - NS * 64;      // 0..64*NP-1 on prep waves
+
+    const int tile = blockIdx.x % p.n_tiles;
+    const int bh = blockIdx.x / p.n_tiles;
+    const int T = p.T, dv = p.dv;
+    const int nchunks = (T + C - 1) / C;
+    const __bf16* kb = reinterpret_cast<const __bf16*>(p.k) + (size_t)bh * T * DK;
+    const __bf16* qb = reinterpret_cast<const __bf16*>(p.q) + (size_t)bh * T * DK;
+    const __bf16* vb = reinterpret_cast<const __bf16*>(p.v) + (size_t)bh * T * dv;
+    const float* ab = p.alpha ? p.alpha + (size_t)bh * T : nullptr;
+    const float* bb = p.beta + (size_t)bh * T;
+    const int col0 = tile * DVT + 16 * wave;  // scan waves: first value column of this wave
+
+    // upper parts of the score and block matrices stay zero
+    for (int i = tid; i < C * L::CP; i += NTHR) {
+        (&s.Ph[0][0])[i] = (__bf16)0.f;
+        (&s.Pl[0][0])[i] = (__bf16)0.f;
+    }
+    for (int i = tid; i < NT * NT * 16 * 24; i += NTHR) {
+        (&s.Bh[0][0][0][0])[i] = (__bf16)0.f;
+        (&s.Bl[0][0][0][0])[i] = (__bf16)0.f;
+    }
+
+    // Each role runs its own loop; both execute two workgroup barriers per
+    // chunk (plus two in the prologue), so the barriers pair up by count.
+    if (!scan) {
+        // ============================ prep waves ============================
+        // Staging registers: chunk cc + 1 is loaded during chunk cc and
+        // written to LDS in the next iteration.  Keys are assigned row-fastest
+        // (one row per lane) so that the transposed copy is written in
+        // contiguous runs; queries use the row-major order.
+        uint4 stK[NKV], stQ[NKV];
+        float stA = 1.f, stB = 0.f;
+        f32x4 gacc[MAXJ];
+
+        auto prep_load = [&](int cc) {
+            const int t0 = cc * C, Lc = min(C, T - t0);
+            static_for<0, NKV>([&](auto I) {
+                constexpr int i = decltype(I)::value;
+                const int vi = plane + i * 64 * NP;
+                {
+                    const int r = min(vi % C, Lc - 1), c8 = (vi / C) * 8;
+                    stK[i] = *reinterpret_cast<const uint4*>(kb + (size_t)(t0 + r) * DK + c8);
+                }
+                {
+                    const int r = min(vi / (DK / 8), Lc - 1), c8 = (vi % (DK / 8)) * 8;
+                    stQ[i] = *reinterpret_cast<const uint4*>(qb + (size_t)(t0 + r) * DK + c8);
+                }
+            });
+            if (pw == 0) {
+                const int tt = t0 + min(lane, Lc - 1);
+                stA = ab ? ab[tt] : 1.f;
+                stB = bb[tt];
+            }
+        };
+        auto prep_store = [&](int cc) {
+            const int buf = cc & 1;
+            const int Lc = min(C, T - cc * C);
+            static_for<0, NKV>([&](auto I) {
+                constexpr int i = decltype(I)::value;
+                const int vi = plane + i * 64 * NP;
+                {
+                    const int r = vi % C, c8 = (vi / C) * 8;
+                    // rows past the end of the sequence are zeroed (value mask)
+                    const unsigned m = r < Lc ? 0xffffffffu : 0u;
+                    const uint4 kv = make_uint4(stK[i].x & m, stK[i].y & m, stK[i].z & m, stK[i].w & m);
+                    *reinterpret_cast<uint4*>(&s.K[buf][r][c8]) = kv;
+                    static_for<0, 8>([&](auto X) {
+                        constexpr int x = decltype(X)::value;
+                        const unsigned word = x < 2 ? kv.x : x < 4 ? kv.y : x < 6 ? kv.z : kv.w;
+                        *reinterpret_cast<unsigned short*>(&s.Kt[buf][c8 + x][r]) =
+                            (unsigned short)(word >> (16 * (x & 1)));
+                    });
+                }
+                {
+                    const int r = vi / (DK / 8), c8 = (vi % (DK / 8)) * 8;
+                    const unsigned m = r < Lc ? 0xffffffffu : 0u;
+                    *reinterpret_cast<uint4*>(&s.Q[buf][r][c8]) =
+                        make_uint4(stQ[i].x & m, stQ[i].y & m, stQ[i].z & m, stQ[i].w & m);
+                }
+            });
+            if (pw == 0) {
+                // padding tokens: alpha = 1, beta = 0 (identity transitions)
+                const float a = lane < Lc ? stA : 1.f;
+                const float l2 = (lane < C) ? __builtin_amdgcn_logf(a) : 0.f;
+                const float g = wave_inclusive_scan(l2, lane);
+                const float gl = __shfl(g, C - 1, 64);
+                if (lane < C) {
+                    s.g2[buf][lane] = g;
+                    s.eg[buf][lane] = __builtin_amdgcn_exp2f(g);
+                    s.dec[buf][lane] = __builtin_amdgcn_exp2f(gl - g);
+                    s.beta[buf][lane] = lane < Lc ? stB : 0.f;
+                }
+                if (lane == 0) s.glast[buf] = __builtin_amdgcn_exp2f(gl);
+            }
+        };
+        // Gram / score tiles: lane holds row r = 16 rt + n, columns 16 ct + 4 h + e.
+        auto gram = [&](auto W, int cc) {
+            constexpr int w = decltype(W)::value;
+            const int buf = cc & 1;
+            static_for<0, J::count(w)>([&](auto JJ) {
+                constexpr int j = decltype(JJ)::value;
+                constexpr int code = J::job(w, j);
+                constexpr int kind = code >> 16;
+                constexpr int rt = (code >> 8) & 255, ct = code & 255;
+                const __bf16* arow = &s.K[buf][16 * ct + n][0];
+                const __bf16* brow = kind == 2 ? &s.Q[buf][16 * rt + n][0] : &s.K[buf][16 * rt + n][0];
+                f32x4 acc = zero4();
+#pragma unroll
+                for (int ss = 0; ss < DK / 32; ++ss)
+                    acc = mfma_bf16(ld_nat8(arow, ss, h), ld_nat8(brow, ss, h), acc);
+                gacc[j] = acc;
+            });
+        };
+        // A_ri = -beta_r exp(g_r - g_i) k_r.k_i (i < r), P_ri = exp(g_r - g_i) q_r.k_i (i <= r)
+        auto form = [&](auto W, int cc) {
+            constexpr int w = decltype(W)::value;
+            const int buf = cc & 1;
+            static_for<0, J::count(w)>([&](auto JJ) {
+                constexpr int j = decltype(JJ)::value;
+                constexpr int code = J::job(w, j);
+                constexpr int kind = code >> 16;
+                constexpr int rt = (code >> 8) & 255, ct = code & 255;
+                const int r = 16 * rt + n;
+                const int i0 = 16 * ct + 4 * h;
+                const float g2r = s.g2[buf][r];
+                const float br = s.beta[buf][r];
+                const f32x4 g2i = *reinterpret_cast<const f32x4*>(&s.g2[buf][i0]);
+                f32x4 v;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float d = __builtin_amdgcn_exp2f(g2r - g2i[e]);
+                    const int i = i0 + e;
+                    if constexpr (kind == 2) v[e] = (i <= r) ? d * gacc[j][e] : 0.f;
+                    else if constexpr (kind == 0) v[e] = (i < r) ? -br * d * gacc[j][e] : 0.f;
+                    else v[e] = -br * d * gacc[j][e];
+                }
+                if constexpr (kind == 2) {
+                    bf16x4 hi, lo;
+                    split4(v, hi, lo);
+                    *reinterpret_cast<bf16x4*>(&s.Ph[r][i0]) = hi;
+                    *reinterpret_cast<bf16x4*>(&s.Pl[r][i0]) = lo;
+                } else if constexpr (kind == 0) {
+                    *reinterpret_cast<f32x4*>(&s.Add[rt][n][4 * h]) = v;
+                } else {
+                    bf16x4 hi, lo;
+                    split4(v, hi, lo);
+                    *reinterpret_cast<bf16x4*>(&s.Bh[rt][ct][n][4 * h]) = hi;
+                    *reinterpret_cast<bf16x4*>(&s.Bl[rt][ct][n][4 * h]) = lo;
+                }
+            });
+        };
+        // T_bb = (I - A_bb)^{-1} for block b: lane jj runs forward
+        // substitution down column jj (rows read four at a time).
+        auto diag_solve = [&](int b) {
+            if (lane < 16) {
+                const int jj = lane;
+                float t[16];
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    float acc = (i == jj) ? 1.f : 0.f;
+#pragma unroll
+                    for (int q = 0; q < (i + 3) / 4; ++q) {
+                        const f32x4 a = *reinterpret_cast<const f32x4*>(&s.Add[b][i][4 * q]);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            if (4 * q + e < i) acc = fmaf(a[e], t[4 * q + e], acc);
+                    }
+                    t[i] = acc;
+                }
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    __bf16 hi, lo;
+                    split_bf16(t[i], hi, lo);
+                    s.Bh[b][b][i][jj] = hi;
+                    s.Bl[b][b][i][jj] = lo;
+                }
+            }
+        };
+        auto by_wave = [&](auto&& f) {
+            switch (pw) {
+                case 0: f(std::integral_constant<int, 0>{}); break;
+                case 1: f(std::integral_constant<int, 1>{}); break;
+                case 2: f(std::integral_constant<int, 2>{}); break;
+                default: f(std::integral_constant<int, 3>{}); break;
+            }
+        };
+
+        prep_load(0);
+        prep_store(0);
+        if (nchunks > 1) prep_load(1);
+        __syncthreads();
+        by_wave([&](auto W) { gram(W, 0); });
+        __syncthreads();
+        for (int c = 0; c < nchunks; ++c) {
+            // ---- phase A ----
+            by_wave([&](auto W) { form(W, c); });
+            if (pw < NT) {
+                wave_lds_sync();
+                diag_solve(pw);
+            }
+            if (c + 1 < nchunks) {
+                prep_store(c + 1);
+                if (c + 2 < nchunks) prep_load(c + 2);
+            }
+            __syncthreads();
+            // ---- phase B ----
+            if (c + 1 < nchunks) by_wave([&](auto W) { gram(W, c + 1); });
+            __syncthreads();
+        }
+    } else {
+        // ============================ scan waves ============================
+        f32x4 Sacc[NK];           // Sacc[t][j] = S[col0 + n][16 t + 4 h + j]
+        __bf16 vnext[NT][4];      // this lane's values of the next chunk, raw (zeroed at use)
+        auto load_v = [&](int cc) {
+            const int t0 = cc * C, Lc = min(C, T - t0);
+            static_for<0, NT>([&](auto RT) {
+                constexpr int rt = decltype(RT)::value;
+                static_for<0, 4>([&](auto JJ) {
+                    constexpr int j = decltype(JJ)::value;
+                    const int r = min(16 * rt + 4 * h + j, Lc - 1);
+                    vnext[rt][j] = vb[(size_t)(t0 + r) * dv + col0 + n];
+                });
+            });
+        };
+        const size_t sb = (size_t)bh * dv * DK + (size_t)(col0 + n) * DK;
+#pragma unroll
+        for (int t = 0; t < NK; ++t)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) Sacc[t][j] = p.S0 ? p.S0[sb + 16 * t + 4 * h + j] : 0.f;
+        load_v(0);
+        __syncthreads();
+        __syncthreads();
+        for (int c = 0; c < nchunks; ++c) {
+            const int buf = c & 1;
+            const int t0 = c * C;
+            const int Lc = min(C, T - t0);
+            // ---- phase A: X = K S^T, Z^T = S Q^T ----
+            f32x4 X[NT], Zt[NT];
+#pragma unroll
+            for (int rt = 0; rt < NT; ++rt) { X[rt] = zero4(); Zt[rt] = zero4(); }
+#pragma unroll
+            for (int ss = 0; ss < DK / 32; ++ss) {
+                bf16x8 shi, slo;
+                split8(Sacc[2 * ss], Sacc[2 * ss + 1], shi, slo);
+                bf16x8 kf[NT], qf[NT];
+#pragma unroll
+                for (int rt = 0; rt < NT; ++rt) {
+                    kf[rt] = ld_perm8(&s.K[buf][16 * rt + n][0], ss, h);
+                    qf[rt] = ld_perm8(&s.Q[buf][16 * rt + n][0], ss, h);
+                }
+#pragma unroll
+                for (int rt = 0; rt < NT; ++rt) X[rt] = mfma_bf16(kf[rt], shi, X[rt]);
+#pragma unroll
+                for (int rt = 0; rt < NT; ++rt) Zt[rt] = mfma_bf16(shi, qf[rt], Zt[rt]);
+#pragma unroll
+                for (int rt = 0; rt < NT; ++rt) X[rt] = mfma_bf16(kf[rt], slo, X[rt]);
+#pragma unroll
+                for (int rt = 0; rt < NT; ++rt) Zt[rt] = mfma_bf16(slo, qf[rt], Zt[rt]);
+            }
+            __syncthreads();
+            // ---- phase B: block forward substitution for V' ----
+            f32x4 Vp[NT];
+            bf16x4 vph[NT], vpl[NT];
+#pragma unroll
+            for (int b = 0; b < NT; ++b) {
+                f32x4 y;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int r = 16 * b + 4 * h + j;
+                    const float vv = r < Lc ? (float)vnext[b][j] : 0.f;
+                    y[j] = s.beta[buf][r] * (vv - s.eg[buf][r] * X[b][j]);
+                }
+                f32x4 a1 = zero4(), a2 = zero4(), a3 = zero4();
+#pragma unroll
+                for (int cb = 0; cb < b; ++cb) {
+                    const bf16x4 ah = *reinterpret_cast<const bf16x4*>(&s.Bh[b][cb][n][4 * h]);
+                    const bf16x4 al = *reinterpret_cast<const bf16x4*>(&s.Bl[b][cb][n][4 * h]);
+                    a1 = mfma16_bf16(ah, vph[cb], a1);
+                    a2 = mfma16_bf16(ah, vpl[cb], a2);
+                    a3 = mfma16_bf16(al, vph[cb], a3);
+                }
+                const f32x4 rhs = y + a1 + a2 + a3;
+                bf16x4 rh, rl;
+                split4(rhs, rh, rl);
+                const bf16x4 th = *reinterpret_cast<const bf16x4*>(&s.Bh[b][b][n][4 * h]);
+                const bf16x4 tl = *reinterpret_cast<const bf16x4*>(&s.Bl[b][b][n][4 * h]);
+                const f32x4 t1 = mfma16_bf16(th, rh, zero4());
+                const f32x4 t2 = mfma16_bf16(th, rl, zero4());
+                const f32x4 t3 = mfma16_bf16(tl, rh, zero4());
+                Vp[b] = t1 + t2 + t3;
+                split4(Vp[b], vph[b], vpl[b]);
+            }
+            if (c + 1 < nchunks) load_v(c + 1);
+            // ---- O^T = diag(exp g) Z^T + V'^T P^T (lane: row 16 rt + n, 4 columns) ----
+            f32x4 PVt[NT];
+#pragma unroll
+            for (int rt = 0; rt < NT; ++rt) PVt[rt] = zero4();
+#pragma unroll
+            for (int ss = 0; ss < C / 32; ++ss) {
+                bf16x8 vhi, vlo;
+                split8(Vp[2 * ss], Vp[2 * ss + 1], vhi, vlo);
+                bf16x8 ph[NT], pl[NT];
+#pragma unroll
+                for (int rt = 0; rt < NT; ++rt) {
+                    if (32 * ss > 16 * rt + 15) continue;   // above the diagonal
+                    ph[rt] = ld_perm8(&s.Ph[16 * rt + n][0], ss, h);
+                    pl[rt] = ld_perm8(&s.Pl[16 * rt + n][0], ss, h);
+                }
+#pragma unroll
+                for (int rt = 0; rt < NT; ++rt)
+                    if (32 * ss <= 16 * rt + 15) PVt[rt] = mfma_bf16(vhi, ph[rt], PVt[rt]);
+#pragma unroll
+                for (int rt = 0; rt < NT; ++rt)
+                    if (32 * ss <= 16 * rt + 15) PVt[rt] = mfma_bf16(vlo, ph[rt], PVt[rt]);
+#pragma unroll
+                for (int rt = 0; rt < NT; ++rt)
+                    if (32 * ss <= 16 * rt + 15) PVt[rt] = mfma_bf16(vhi, pl[rt], PVt[rt]);
+            }
+#pragma unroll
+            for (int rt = 0; rt < NT; ++rt) {
+                const int r = 16 * rt + n;
+                if (r < Lc) {
+                    const float e = s.eg[buf][r];
+                    const f32x4 o = e * Zt[rt] + PVt[rt];
+                    const size_t off = ((size_t)bh * T + t0 + r) * dv + col0 + 4 * h;
+                    if (p.o_bf16)
+                        *reinterpret_cast<bf16x4*>(reinterpret_cast<__bf16*>(p.O) + off) =
+                            __builtin_convertvector(o, bf16x4);
+                    else
+                        *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(p.O) + off) = o;
+                }
+            }
+            // ---- S^T <- exp(g_last) S^T + K^T diag(exp(g_last - g)) V' ----
+            const float gl = s.glast[buf];
+#pragma unroll
+            for (int t = 0; t < NK; ++t) Sacc[t] *= gl;
+            f32x4 Vd[NT];
+#pragma unroll
+            for (int rt = 0; rt < NT; ++rt)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) Vd[rt][j] = s.dec[buf][16 * rt + 4 * h + j] * Vp[rt][j];
+#pragma unroll
+            for (int ss = 0; ss < C / 32; ++ss) {
+                bf16x8 vhi, vlo;
+                split8(Vd[2 * ss], Vd[2 * ss + 1], vhi, vlo);
+                bf16x8 kt[NK];
+#pragma unroll
+                for (int t = 0; t < NK; ++t) kt[t] = ld_perm8(&s.Kt[buf][16 * t + n][0], ss, h);
+#pragma unroll
+                for (int t = 0; t < NK; ++t) Sacc[t] = mfma_bf16(kt[t], vhi, Sacc[t]);
+#pragma unroll
+                for (int t = 0; t < NK; ++t) Sacc[t] = mfma_bf16(kt[t], vlo, Sacc[t]);
+            }
+            __syncthreads();
+        }
+#pragma unroll
+        for (int t = 0; t < NK; ++t)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) p.S_final[sb + 16 * t + 4 * h + j] = Sacc[t][j];
+    }
+}
+
+}  // namespace gdn
