@@ -206,6 +206,7 @@ gdn_status gdn_chunk_fwd(const gdn_shape* s, const void* q, const void* k, const
     p.dv = s->d_v;
     p.n_tiles = s->d_v / (16 * nw);
     p.o_bf16 = s->o_dtype == GDN_BF16;
+    p.xcd_groups = piped && ((long)s->B * s->H) % 8 == 0;
     const long nblocks = (long)s->B * s->H * p.n_tiles;
     if (nblocks > 0x7fffffffL) return fail(GDN_ERR_BAD_SHAPE, "grid too large");
     launch(p, nblocks, reinterpret_cast<hipStream_t>(stream));

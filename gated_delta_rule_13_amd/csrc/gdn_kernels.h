@@ -42,6 +42,7 @@ struct FwdParams {
     int B, H, T, dv;
     int n_tiles;          // value-column tiles per head
     int o_bf16;           // O stored as bf16 (else fp32)
+    int xcd_groups;       // pipelined kernel: place a head's tiles on one XCD
 };
 
 // LDS layout of one workgroup.  Rows are padded by 16 bytes.

@@ -81,8 +81,11 @@ struct alignas(16) PipeLds {
     __bf16 Pl[C][CP];                   //                        lo
     __bf16 Bh[NT][NT][16][24];          // [b][c<b]: A_bc, [b][b]: T_bb (hi)
     __bf16 Bl[NT][NT][16][24];          //                               (lo)
-    float Add[NT][16][20];              // diagonal blocks of A, fp32 (16-byte rows)
+    float Adt[NT][16][16];              // diagonal blocks of A, fp32, transposed: [b][k][i] = A_b[i][k]
     float g2[2][C];                     // inclusive cumsum of log2 alpha
+    float er[2][C];                     // 2^(g2_r - g2_ref): row factor of exp(g_r - g_i)
+    float fi[2][C];                     // 2^(g2_ref - g2_i): column factor
+    int sep[2];                         // row x column factors safe in fp32 for this chunk
     float eg[2][C];                     // 2^g2 = exp(g)
     float dec[2][C];                    // exp(g_last - g)
     float beta[2][C];
@@ -91,9 +94,9 @@ struct alignas(16) PipeLds {
 
 // Chunk-local tile jobs of the prep waves.  Kinds: 0 = diagonal block of A
 // (kept fp32 for the diagonal solve), 1 = off-diagonal block of A, 2 = block
-// of the masked scores P.  Prep wave w < NT takes diagonal block w (and then
-// solves it); the other blocks go round-robin.  Encoding:
-// (kind << 16) | (rt << 8) | ct for tile (rt, ct), ct <= rt.
+// of the masked scores P.  Prep wave 0 takes every diagonal block (it also
+// solves them); the other blocks go round-robin over waves 1..NP-1.
+// Encoding: (kind << 16) | (rt << 8) | ct for tile (rt, ct), ct <= rt.
 template <int NT, int NP>
 struct PrepJobs {
     static constexpr int NPAIR = NT * (NT + 1) / 2;
@@ -127,17 +130,15 @@ struct PrepJobs {
         const int q = k - NOFF;
         return (2 << 16) | (pair_rt(q) << 8) | pair_ct(q);
     }
-    static constexpr int owner(int k) { return (NT + k) % NP; }
+    static constexpr int owner(int k) { return 1 + k % (NP - 1); }
     static constexpr int count(int w) {
-        int n = w < NT ? 1 : 0;
+        if (w == 0) return NT;
+        int n = 0;
         for (int k = 0; k < NREST; ++k) n += owner(k) == w;
         return n;
     }
     static constexpr int job(int w, int j) {
-        if (w < NT) {
-            if (j == 0) return (w << 8) | w;
-            --j;
-        }
+        if (w == 0) return (j << 8) | j;
         for (int k = 0; k < NREST; ++k)
             if (owner(k) == w) {
                 if (j == 0) return rest(k);
@@ -178,8 +179,18 @@ __global__ __launch_bounds__((NS + kPrepWaves) * 64) void gdn_fwd_pipe_kernel(Fw
     const int pw = wave - NS;             // prep wave 0..NP-1
     const int plane = tid - NS * 64;      // 0..64*NP-1 on prep waves
 
-    const int tile = blockIdx.x % p.n_tiles;
-    const int bh = blockIdx.x / p.n_tiles;
+    // Workgroups are dispatched round-robin over the 8 XCDs (L2 domains);
+    // when the head count allows it, all value tiles of one head get block
+    // ids congruent mod 8, so they share that XCD's L2 copy of K and Q.
+    int tile, bh;
+    if (p.xcd_groups) {
+        const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+        tile = slot % p.n_tiles;
+        bh = xcd + 8 * (slot / p.n_tiles);
+    } else {
+        tile = blockIdx.x % p.n_tiles;
+        bh = blockIdx.x / p.n_tiles;
+    }
     const int T = p.T, dv = p.dv;
     const int nchunks = (T + C - 1) / C;
     const __bf16* kb = reinterpret_cast<const __bf16*>(p.k) + (size_t)bh * T * DK;
@@ -203,35 +214,37 @@ __global__ __launch_bounds__((NS + kPrepWaves) * 64) void gdn_fwd_pipe_kernel(Fw
     // chunk (plus two in the prologue), so the barriers pair up by count.
     if (!scan) {
         // ============================ prep waves ============================
-        // Staging registers: chunk cc + 1 is loaded during chunk cc and
-        // written to LDS in the next iteration.  Keys are assigned row-fastest
-        // (one row per lane) so that the transposed copy is written in
-        // contiguous runs; queries use the row-major order.
-        uint4 stK[NKV], stQ[NKV];
-        float stA = 1.f, stB = 0.f;
+        // Staging registers, two sets by chunk parity: chunk cc is loaded into
+        // set cc & 1 two iterations before it is written to LDS.  Keys are
+        // assigned row-fastest (one row per lane) so that the transposed copy
+        // is written in contiguous runs; queries use the row-major order.
+        uint4 stK[2][NKV], stQ[2][NKV];
+        float stA[2] = {1.f, 1.f}, stB[2] = {0.f, 0.f};
         f32x4 gacc[MAXJ];
 
-        auto prep_load = [&](int cc) {
+        auto prep_load = [&](auto PAR, int cc) __attribute__((always_inline)) {
+            constexpr int par = decltype(PAR)::value;
             const int t0 = cc * C, Lc = min(C, T - t0);
             static_for<0, NKV>([&](auto I) {
                 constexpr int i = decltype(I)::value;
                 const int vi = plane + i * 64 * NP;
                 {
                     const int r = min(vi % C, Lc - 1), c8 = (vi / C) * 8;
-                    stK[i] = *reinterpret_cast<const uint4*>(kb + (size_t)(t0 + r) * DK + c8);
+                    stK[par][i] = *reinterpret_cast<const uint4*>(kb + (size_t)(t0 + r) * DK + c8);
                 }
                 {
                     const int r = min(vi / (DK / 8), Lc - 1), c8 = (vi % (DK / 8)) * 8;
-                    stQ[i] = *reinterpret_cast<const uint4*>(qb + (size_t)(t0 + r) * DK + c8);
+                    stQ[par][i] = *reinterpret_cast<const uint4*>(qb + (size_t)(t0 + r) * DK + c8);
                 }
             });
             if (pw == 0) {
                 const int tt = t0 + min(lane, Lc - 1);
-                stA = ab ? ab[tt] : 1.f;
-                stB = bb[tt];
+                stA[par] = ab ? ab[tt] : 1.f;
+                stB[par] = bb[tt];
             }
         };
-        auto prep_store = [&](int cc) {
+        auto prep_store = [&](auto PAR, int cc) __attribute__((always_inline)) {
+            constexpr int par = decltype(PAR)::value;
             const int buf = cc & 1;
             const int Lc = min(C, T - cc * C);
             static_for<0, NKV>([&](auto I) {
@@ -241,7 +254,8 @@ __global__ __launch_bounds__((NS + kPrepWaves) * 64) void gdn_fwd_pipe_kernel(Fw
                     const int r = vi % C, c8 = (vi / C) * 8;
                     // rows past the end of the sequence are zeroed (value mask)
                     const unsigned m = r < Lc ? 0xffffffffu : 0u;
-                    const uint4 kv = make_uint4(stK[i].x & m, stK[i].y & m, stK[i].z & m, stK[i].w & m);
+                    const uint4 sv = stK[par][i];
+                    const uint4 kv = make_uint4(sv.x & m, sv.y & m, sv.z & m, sv.w & m);
                     *reinterpret_cast<uint4*>(&s.K[buf][r][c8]) = kv;
                     static_for<0, 8>([&](auto X) {
                         constexpr int x = decltype(X)::value;
@@ -253,27 +267,38 @@ __global__ __launch_bounds__((NS + kPrepWaves) * 64) void gdn_fwd_pipe_kernel(Fw
                 {
                     const int r = vi / (DK / 8), c8 = (vi % (DK / 8)) * 8;
                     const unsigned m = r < Lc ? 0xffffffffu : 0u;
+                    const uint4 sv = stQ[par][i];
                     *reinterpret_cast<uint4*>(&s.Q[buf][r][c8]) =
-                        make_uint4(stQ[i].x & m, stQ[i].y & m, stQ[i].z & m, stQ[i].w & m);
+                        make_uint4(sv.x & m, sv.y & m, sv.z & m, sv.w & m);
                 }
             });
             if (pw == 0) {
                 // padding tokens: alpha = 1, beta = 0 (identity transitions)
-                const float a = lane < Lc ? stA : 1.f;
+                const float a = lane < Lc ? stA[par] : 1.f;
                 const float l2 = (lane < C) ? __builtin_amdgcn_logf(a) : 0.f;
                 const float g = wave_inclusive_scan(l2, lane);
                 const float gl = __shfl(g, C - 1, 64);
+                // exp(g_r - g_i) = 2^(g2_r - ref) * 2^(ref - g2_i) with ref the middle
+                // of the chunk; used when the chunk's decay range keeps both factors
+                // far inside fp32 (else the formation exponentiates each ratio).
+                const float ref = __shfl(g, C / 2, 64);
+                const float g0 = __shfl(g, 0, 64);
                 if (lane < C) {
                     s.g2[buf][lane] = g;
                     s.eg[buf][lane] = __builtin_amdgcn_exp2f(g);
                     s.dec[buf][lane] = __builtin_amdgcn_exp2f(gl - g);
-                    s.beta[buf][lane] = lane < Lc ? stB : 0.f;
+                    s.beta[buf][lane] = lane < Lc ? stB[par] : 0.f;
+                    s.er[buf][lane] = __builtin_amdgcn_exp2f(g - ref);
+                    s.fi[buf][lane] = __builtin_amdgcn_exp2f(ref - g);
                 }
-                if (lane == 0) s.glast[buf] = __builtin_amdgcn_exp2f(gl);
+                if (lane == 0) {
+                    s.glast[buf] = __builtin_amdgcn_exp2f(gl);
+                    s.sep[buf] = (g0 - gl) <= 96.f;
+                }
             }
         };
         // Gram / score tiles: lane holds row r = 16 rt + n, columns 16 ct + 4 h + e.
-        auto gram = [&](auto W, int cc) {
+        auto gram = [&](auto W, int cc) __attribute__((always_inline)) {
             constexpr int w = decltype(W)::value;
             const int buf = cc & 1;
             static_for<0, J::count(w)>([&](auto JJ) {
@@ -290,9 +315,11 @@ __global__ __launch_bounds__((NS + kPrepWaves) * 64) void gdn_fwd_pipe_kernel(Fw
                 gacc[j] = acc;
             });
         };
-        // A_ri = -beta_r exp(g_r - g_i) k_r.k_i (i < r), P_ri = exp(g_r - g_i) q_r.k_i (i <= r)
-        auto form = [&](auto W, int cc) {
+        // A_ri = -beta_r exp(g_r - g_i) k_r.k_i (i < r), P_ri = exp(g_r - g_i) q_r.k_i (i <= r).
+        // SEP: exp(g_r - g_i) from the separable row / column factors.
+        auto form = [&](auto W, auto SEP, int cc) __attribute__((always_inline)) {
             constexpr int w = decltype(W)::value;
+            constexpr bool sep = decltype(SEP)::value;
             const int buf = cc & 1;
             static_for<0, J::count(w)>([&](auto JJ) {
                 constexpr int j = decltype(JJ)::value;
@@ -301,17 +328,23 @@ __global__ __launch_bounds__((NS + kPrepWaves) * 64) void gdn_fwd_pipe_kernel(Fw
                 constexpr int rt = (code >> 8) & 255, ct = code & 255;
                 const int r = 16 * rt + n;
                 const int i0 = 16 * ct + 4 * h;
-                const float g2r = s.g2[buf][r];
                 const float br = s.beta[buf][r];
-                const f32x4 g2i = *reinterpret_cast<const f32x4*>(&s.g2[buf][i0]);
+                f32x4 d;
+                if constexpr (sep) {
+                    d = s.er[buf][r] * *reinterpret_cast<const f32x4*>(&s.fi[buf][i0]);
+                } else {
+                    const float g2r = s.g2[buf][r];
+                    const f32x4 g2i = *reinterpret_cast<const f32x4*>(&s.g2[buf][i0]);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) d[e] = __builtin_amdgcn_exp2f(g2r - g2i[e]);
+                }
                 f32x4 v;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const float d = __builtin_amdgcn_exp2f(g2r - g2i[e]);
                     const int i = i0 + e;
-                    if constexpr (kind == 2) v[e] = (i <= r) ? d * gacc[j][e] : 0.f;
-                    else if constexpr (kind == 0) v[e] = (i < r) ? -br * d * gacc[j][e] : 0.f;
-                    else v[e] = -br * d * gacc[j][e];
+                    if constexpr (kind == 2) v[e] = (i <= r) ? d[e] * gacc[j][e] : 0.f;
+                    else if constexpr (kind == 0) v[e] = (i < r) ? -br * d[e] * gacc[j][e] : 0.f;
+                    else v[e] = -br * d[e] * gacc[j][e];
                 }
                 if constexpr (kind == 2) {
                     bf16x4 hi, lo;
@@ -319,7 +352,9 @@ __global__ __launch_bounds__((NS + kPrepWaves) * 64) void gdn_fwd_pipe_kernel(Fw
                     *reinterpret_cast<bf16x4*>(&s.Ph[r][i0]) = hi;
                     *reinterpret_cast<bf16x4*>(&s.Pl[r][i0]) = lo;
                 } else if constexpr (kind == 0) {
-                    *reinterpret_cast<f32x4*>(&s.Add[rt][n][4 * h]) = v;
+                    // element (row n, column 4h + e) of diagonal block rt, transposed
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) s.Adt[rt][4 * h + e][n] = v[e];
                 } else {
                     bf16x4 hi, lo;
                     split4(v, hi, lo);
@@ -328,23 +363,27 @@ __global__ __launch_bounds__((NS + kPrepWaves) * 64) void gdn_fwd_pipe_kernel(Fw
                 }
             });
         };
-        // T_bb = (I - A_bb)^{-1} for block b: lane jj runs forward
-        // substitution down column jj (rows read four at a time).
-        auto diag_solve = [&](int b) {
-            if (lane < 16) {
-                const int jj = lane;
+        // T_bb = (I - A_bb)^{-1}, all diagonal blocks at once: lane (b, jj)
+        // runs forward substitution down column jj of block b, right-looking:
+        // once T[k][jj] is final it is added into every later row's partial
+        // sum, so only one multiply-add per row sits on the dependency chain.
+        auto diag_solve = [&]() __attribute__((always_inline)) {
+            if (lane < 16 * NT) {
+                const int b = lane >> 4, jj = lane & 15;
+                float part[16];
+#pragma unroll
+                for (int i = 0; i < 16; ++i) part[i] = 0.f;
                 float t[16];
 #pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    float acc = (i == jj) ? 1.f : 0.f;
+                for (int k = 0; k < 16; ++k) {
+                    t[k] = part[k] + ((k == jj) ? 1.f : 0.f);
 #pragma unroll
-                    for (int q = 0; q < (i + 3) / 4; ++q) {
-                        const f32x4 a = *reinterpret_cast<const f32x4*>(&s.Add[b][i][4 * q]);
+                    for (int q = (k + 1) / 4; q < 4; ++q) {
+                        const f32x4 a = *reinterpret_cast<const f32x4*>(&s.Adt[b][k][4 * q]);
 #pragma unroll
                         for (int e = 0; e < 4; ++e)
-                            if (4 * q + e < i) acc = fmaf(a[e], t[4 * q + e], acc);
+                            if (4 * q + e > k) part[4 * q + e] = fmaf(a[e], t[k], part[4 * q + e]);
                     }
-                    t[i] = acc;
                 }
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
@@ -355,42 +394,52 @@ __global__ __launch_bounds__((NS + kPrepWaves) * 64) void gdn_fwd_pipe_kernel(Fw
                 }
             }
         };
-        auto by_wave = [&](auto&& f) {
-            switch (pw) {
-                case 0: f(std::integral_constant<int, 0>{}); break;
-                case 1: f(std::integral_constant<int, 1>{}); break;
-                case 2: f(std::integral_constant<int, 2>{}); break;
-                default: f(std::integral_constant<int, 3>{}); break;
+        // The whole prep loop is specialised per prep wave so that every tile
+        // job index is a compile-time constant within one loop.
+        auto prep_role = [&](auto W) __attribute__((always_inline)) {
+            constexpr int w = decltype(W)::value;
+            // one pipeline step; PAR = parity of chunk c
+            auto step = [&](auto PAR, int c) __attribute__((always_inline)) {
+                constexpr int nxt = decltype(PAR)::value ^ 1;
+                // ---- phase A: chunk-local matrices of chunk c; stage chunk c + 1 ----
+                if (s.sep[c & 1]) form(W, std::true_type{}, c);
+                else form(W, std::false_type{}, c);
+                if constexpr (w == 0) {
+                    wave_lds_sync();
+                    diag_solve();
+                }
+                if (c + 1 < nchunks) {
+                    prep_store(std::integral_constant<int, nxt>{}, c + 1);
+                    if (c + 3 < nchunks) prep_load(std::integral_constant<int, nxt>{}, c + 3);
+                }
+                __syncthreads();
+                // ---- phase B: Gram matrix and scores of chunk c + 1 ----
+                if (c + 1 < nchunks) gram(W, c + 1);
+                __syncthreads();
+            };
+            prep_load(std::integral_constant<int, 0>{}, 0);
+            if (nchunks > 1) prep_load(std::integral_constant<int, 1>{}, 1);
+            prep_store(std::integral_constant<int, 0>{}, 0);
+            if (nchunks > 2) prep_load(std::integral_constant<int, 0>{}, 2);
+            __syncthreads();
+            gram(W, 0);
+            __syncthreads();
+            for (int c = 0; c < nchunks; c += 2) {
+                step(std::integral_constant<int, 0>{}, c);
+                if (c + 1 < nchunks) step(std::integral_constant<int, 1>{}, c + 1);
             }
         };
-
-        prep_load(0);
-        prep_store(0);
-        if (nchunks > 1) prep_load(1);
-        __syncthreads();
-        by_wave([&](auto W) { gram(W, 0); });
-        __syncthreads();
-        for (int c = 0; c < nchunks; ++c) {
-            // ---- phase A ----
-            by_wave([&](auto W) { form(W, c); });
-            if (pw < NT) {
-                wave_lds_sync();
-                diag_solve(pw);
-            }
-            if (c + 1 < nchunks) {
-                prep_store(c + 1);
-                if (c + 2 < nchunks) prep_load(c + 2);
-            }
-            __syncthreads();
-            // ---- phase B ----
-            if (c + 1 < nchunks) by_wave([&](auto W) { gram(W, c + 1); });
-            __syncthreads();
+        switch (pw) {
+            case 0: prep_role(std::integral_constant<int, 0>{}); break;
+            case 1: prep_role(std::integral_constant<int, 1>{}); break;
+            case 2: prep_role(std::integral_constant<int, 2>{}); break;
+            default: prep_role(std::integral_constant<int, 3>{}); break;
         }
     } else {
         // ============================ scan waves ============================
         f32x4 Sacc[NK];           // Sacc[t][j] = S[col0 + n][16 t + 4 h + j]
         __bf16 vnext[NT][4];      // this lane's values of the next chunk, raw (zeroed at use)
-        auto load_v = [&](int cc) {
+        auto load_v = [&](int cc) __attribute__((always_inline)) {
             const int t0 = cc * C, Lc = min(C, T - t0);
             static_for<0, NT>([&](auto RT) {
                 constexpr int rt = decltype(RT)::value;
@@ -438,6 +487,21 @@ __global__ __launch_bounds__((NS + kPrepWaves) * 64) void gdn_fwd_pipe_kernel(Fw
             }
             __syncthreads();
             // ---- phase B: block forward substitution for V' ----
+            // all operands of the substitution are loaded before the chain starts
+            bf16x4 bh_[NT][NT], bl_[NT][NT];
+#pragma unroll
+            for (int b = 0; b < NT; ++b)
+#pragma unroll
+                for (int cb = 0; cb <= b; ++cb) {
+                    bh_[b][cb] = *reinterpret_cast<const bf16x4*>(&s.Bh[b][cb][n][4 * h]);
+                    bl_[b][cb] = *reinterpret_cast<const bf16x4*>(&s.Bl[b][cb][n][4 * h]);
+                }
+            f32x4 be_[NT], eg_[NT];
+#pragma unroll
+            for (int b = 0; b < NT; ++b) {
+                be_[b] = *reinterpret_cast<const f32x4*>(&s.beta[buf][16 * b + 4 * h]);
+                eg_[b] = *reinterpret_cast<const f32x4*>(&s.eg[buf][16 * b + 4 * h]);
+            }
             f32x4 Vp[NT];
             bf16x4 vph[NT], vpl[NT];
 #pragma unroll
@@ -447,22 +511,20 @@ __global__ __launch_bounds__((NS + kPrepWaves) * 64) void gdn_fwd_pipe_kernel(Fw
                 for (int j = 0; j < 4; ++j) {
                     const int r = 16 * b + 4 * h + j;
                     const float vv = r < Lc ? (float)vnext[b][j] : 0.f;
-                    y[j] = s.beta[buf][r] * (vv - s.eg[buf][r] * X[b][j]);
+                    y[j] = be_[b][j] * (vv - eg_[b][j] * X[b][j]);
                 }
                 f32x4 a1 = zero4(), a2 = zero4(), a3 = zero4();
 #pragma unroll
                 for (int cb = 0; cb < b; ++cb) {
-                    const bf16x4 ah = *reinterpret_cast<const bf16x4*>(&s.Bh[b][cb][n][4 * h]);
-                    const bf16x4 al = *reinterpret_cast<const bf16x4*>(&s.Bl[b][cb][n][4 * h]);
-                    a1 = mfma16_bf16(ah, vph[cb], a1);
-                    a2 = mfma16_bf16(ah, vpl[cb], a2);
-                    a3 = mfma16_bf16(al, vph[cb], a3);
+                    a1 = mfma16_bf16(bh_[b][cb], vph[cb], a1);
+                    a2 = mfma16_bf16(bh_[b][cb], vpl[cb], a2);
+                    a3 = mfma16_bf16(bl_[b][cb], vph[cb], a3);
                 }
                 const f32x4 rhs = y + a1 + a2 + a3;
                 bf16x4 rh, rl;
                 split4(rhs, rh, rl);
-                const bf16x4 th = *reinterpret_cast<const bf16x4*>(&s.Bh[b][b][n][4 * h]);
-                const bf16x4 tl = *reinterpret_cast<const bf16x4*>(&s.Bl[b][b][n][4 * h]);
+                const bf16x4 th = bh_[b][b];
+                const bf16x4 tl = bl_[b][b];
                 const f32x4 t1 = mfma16_bf16(th, rh, zero4());
                 const f32x4 t2 = mfma16_bf16(th, rl, zero4());
                 const f32x4 t3 = mfma16_bf16(tl, rh, zero4());
