@@ -18,15 +18,15 @@
 //    value columns and that slice of the fp32 state (S^T in MFMA
 //    accumulators); NP = 4 "prep" waves build the next chunk's chunk-local
 //    quantities (decay prefix, Gram matrix, masked scores, diagonal-block
-//    solves) while the scan waves consume the current chunk.  Per chunk:
-//       phase A: scan  X = K S^T, Z^T = S Q^T
-//                prep  form A / P / T_bb of this chunk, stage the next one
-//       phase B: scan  block substitution for V', O^T = Z^T + V'^T P^T,
-//                      state update
-//                prep  Gram matrix and scores of the next chunk (MFMA)
-//    Keys, queries and transposed keys are double-buffered in LDS.  The
-//    output products are taken transposed (operands swapped) so that each
-//    lane ends with four consecutive columns of one output row.
+//    solves) while the scan waves consume the current chunk.  Per chunk c:
+//       phase A: scan  X = K S^T, Z^T = S Q^T, block substitution for V'
+//                prep  masked scores P of chunk c; stage chunk c + 1
+//       phase B: scan  O^T = Z^T + V'^T P^T, state update
+//                prep  Gram matrix of chunk c + 1 (MFMA), its A blocks and
+//                      diagonal-block solves T_bb
+//    Keys, queries, transposed keys and the block matrices are double-buffered
+//    in LDS.  The output products are taken transposed (operands swapped) so
+//    that each lane ends with four consecutive columns of one output row.
 //
 // Precision: as in gdn_kernels.h -- inputs exact in bf16, every derived MFMA
 // operand split into bf16 hi + lo, fp32 accumulation and fp32 state.
@@ -79,8 +79,11 @@ struct alignas(16) PipeLds {
     __bf16 Kt[2][DK][CP];
     __bf16 Ph[C][CP];                   // masked decayed scores, hi
     __bf16 Pl[C][CP];                   //                        lo
-    __bf16 Bh[NT][NT][16][24];          // [b][c<b]: A_bc, [b][b]: T_bb (hi)
-    __bf16 Bl[NT][NT][16][24];          //                               (lo)
+    static constexpr int NB = NT * (NT + 1) / 2;   // blocks on and below the diagonal
+    static constexpr int bidx(int b, int cb) { return b * (b + 1) / 2 + cb; }
+    // block matrices by chunk parity: block (b, c<b) holds A_bc, block (b, b) holds T_bb
+    __bf16 Bh[2][NB][16][16];           // hi
+    __bf16 Bl[2][NB][16][16];           // lo
     float Adt[NT][16][16];              // diagonal blocks of A, fp32, transposed: [b][k][i] = A_b[i][k]
     float g2[2][C];                     // inclusive cumsum of log2 alpha
     float er[2][C];                     // 2^(g2_r - g2_ref): row factor of exp(g_r - g_i)
@@ -200,14 +203,10 @@ __global__ __launch_bounds__((NS + kPrepWaves) * 64) void gdn_fwd_pipe_kernel(Fw
     const float* bb = p.beta + (size_t)bh * T;
     const int col0 = tile * DVT + 16 * wave;  // scan waves: first value column of this wave
 
-    // upper parts of the score and block matrices stay zero
+    // the upper part of the score matrix stays zero
     for (int i = tid; i < C * L::CP; i += NTHR) {
         (&s.Ph[0][0])[i] = (__bf16)0.f;
         (&s.Pl[0][0])[i] = (__bf16)0.f;
-    }
-    for (int i = tid; i < NT * NT * 16 * 24; i += NTHR) {
-        (&s.Bh[0][0][0][0])[i] = (__bf16)0.f;
-        (&s.Bl[0][0][0][0])[i] = (__bf16)0.f;
     }
 
     // Each role runs its own loop; both execute two workgroup barriers per
@@ -317,15 +316,18 @@ __global__ __launch_bounds__((NS + kPrepWaves) * 64) void gdn_fwd_pipe_kernel(Fw
         };
         // A_ri = -beta_r exp(g_r - g_i) k_r.k_i (i < r), P_ri = exp(g_r - g_i) q_r.k_i (i <= r).
         // SEP: exp(g_r - g_i) from the separable row / column factors.
-        auto form = [&](auto W, auto SEP, int cc) __attribute__((always_inline)) {
+        // SCORES: form the P blocks (else the A blocks) of this wave's jobs.
+        auto form = [&](auto W, auto SEP, auto SCORES, int cc) __attribute__((always_inline)) {
             constexpr int w = decltype(W)::value;
             constexpr bool sep = decltype(SEP)::value;
+            constexpr bool scores = decltype(SCORES)::value;
             const int buf = cc & 1;
             static_for<0, J::count(w)>([&](auto JJ) {
                 constexpr int j = decltype(JJ)::value;
                 constexpr int code = J::job(w, j);
                 constexpr int kind = code >> 16;
                 constexpr int rt = (code >> 8) & 255, ct = code & 255;
+                if constexpr ((kind == 2) == scores) {
                 const int r = 16 * rt + n;
                 const int i0 = 16 * ct + 4 * h;
                 const float br = s.beta[buf][r];
@@ -358,8 +360,9 @@ __global__ __launch_bounds__((NS + kPrepWaves) * 64) void gdn_fwd_pipe_kernel(Fw
                 } else {
                     bf16x4 hi, lo;
                     split4(v, hi, lo);
-                    *reinterpret_cast<bf16x4*>(&s.Bh[rt][ct][n][4 * h]) = hi;
-                    *reinterpret_cast<bf16x4*>(&s.Bl[rt][ct][n][4 * h]) = lo;
+                    *reinterpret_cast<bf16x4*>(&s.Bh[buf][L::bidx(rt, ct)][n][4 * h]) = hi;
+                    *reinterpret_cast<bf16x4*>(&s.Bl[buf][L::bidx(rt, ct)][n][4 * h]) = lo;
+                }
                 }
             });
         };
@@ -367,7 +370,8 @@ __global__ __launch_bounds__((NS + kPrepWaves) * 64) void gdn_fwd_pipe_kernel(Fw
         // runs forward substitution down column jj of block b, right-looking:
         // once T[k][jj] is final it is added into every later row's partial
         // sum, so only one multiply-add per row sits on the dependency chain.
-        auto diag_solve = [&]() __attribute__((always_inline)) {
+        auto diag_solve = [&](int cc) __attribute__((always_inline)) {
+            const int buf = cc & 1;
             if (lane < 16 * NT) {
                 const int b = lane >> 4, jj = lane & 15;
                 float part[16];
@@ -389,8 +393,8 @@ __global__ __launch_bounds__((NS + kPrepWaves) * 64) void gdn_fwd_pipe_kernel(Fw
                 for (int i = 0; i < 16; ++i) {
                     __bf16 hi, lo;
                     split_bf16(t[i], hi, lo);
-                    s.Bh[b][b][i][jj] = hi;
-                    s.Bl[b][b][i][jj] = lo;
+                    s.Bh[buf][L::bidx(b, b)][i][jj] = hi;
+                    s.Bl[buf][L::bidx(b, b)][i][jj] = lo;
                 }
             }
         };
@@ -398,23 +402,31 @@ __global__ __launch_bounds__((NS + kPrepWaves) * 64) void gdn_fwd_pipe_kernel(Fw
         // job index is a compile-time constant within one loop.
         auto prep_role = [&](auto W) __attribute__((always_inline)) {
             constexpr int w = decltype(W)::value;
+            // Gram tiles of chunk cc, then its A blocks and diagonal solves
+            // (written to the block buffer of cc's parity).  The score tiles
+            // stay in registers until the next phase A.
+            auto chunk_matrices = [&](int cc) __attribute__((always_inline)) {
+                gram(W, cc);
+                if (s.sep[cc & 1]) form(W, std::true_type{}, std::false_type{}, cc);
+                else form(W, std::false_type{}, std::false_type{}, cc);
+                if constexpr (w == 0) {
+                    wave_lds_sync();
+                    diag_solve(cc);
+                }
+            };
             // one pipeline step; PAR = parity of chunk c
             auto step = [&](auto PAR, int c) __attribute__((always_inline)) {
                 constexpr int nxt = decltype(PAR)::value ^ 1;
-                // ---- phase A: chunk-local matrices of chunk c; stage chunk c + 1 ----
-                if (s.sep[c & 1]) form(W, std::true_type{}, c);
-                else form(W, std::false_type{}, c);
-                if constexpr (w == 0) {
-                    wave_lds_sync();
-                    diag_solve();
-                }
+                // ---- phase A: scores of chunk c; stage chunk c + 1 ----
+                if (s.sep[c & 1]) form(W, std::true_type{}, std::true_type{}, c);
+                else form(W, std::false_type{}, std::true_type{}, c);
                 if (c + 1 < nchunks) {
                     prep_store(std::integral_constant<int, nxt>{}, c + 1);
                     if (c + 3 < nchunks) prep_load(std::integral_constant<int, nxt>{}, c + 3);
                 }
                 __syncthreads();
-                // ---- phase B: Gram matrix and scores of chunk c + 1 ----
-                if (c + 1 < nchunks) gram(W, c + 1);
+                // ---- phase B: Gram matrix, A blocks and T_bb of chunk c + 1 ----
+                if (c + 1 < nchunks) chunk_matrices(c + 1);
                 __syncthreads();
             };
             prep_load(std::integral_constant<int, 0>{}, 0);
@@ -422,7 +434,7 @@ __global__ __launch_bounds__((NS + kPrepWaves) * 64) void gdn_fwd_pipe_kernel(Fw
             prep_store(std::integral_constant<int, 0>{}, 0);
             if (nchunks > 2) prep_load(std::integral_constant<int, 0>{}, 2);
             __syncthreads();
-            gram(W, 0);
+            chunk_matrices(0);
             __syncthreads();
             for (int c = 0; c < nchunks; c += 2) {
                 step(std::integral_constant<int, 0>{}, c);
@@ -485,16 +497,15 @@ __global__ __launch_bounds__((NS + kPrepWaves) * 64) void gdn_fwd_pipe_kernel(Fw
 #pragma unroll
                 for (int rt = 0; rt < NT; ++rt) Zt[rt] = mfma_bf16(slo, qf[rt], Zt[rt]);
             }
-            __syncthreads();
-            // ---- phase B: block forward substitution for V' ----
+            // ---- block forward substitution for V' ----
             // all operands of the substitution are loaded before the chain starts
             bf16x4 bh_[NT][NT], bl_[NT][NT];
 #pragma unroll
             for (int b = 0; b < NT; ++b)
 #pragma unroll
                 for (int cb = 0; cb <= b; ++cb) {
-                    bh_[b][cb] = *reinterpret_cast<const bf16x4*>(&s.Bh[b][cb][n][4 * h]);
-                    bl_[b][cb] = *reinterpret_cast<const bf16x4*>(&s.Bl[b][cb][n][4 * h]);
+                    bh_[b][cb] = *reinterpret_cast<const bf16x4*>(&s.Bh[buf][L::bidx(b, cb)][n][4 * h]);
+                    bl_[b][cb] = *reinterpret_cast<const bf16x4*>(&s.Bl[buf][L::bidx(b, cb)][n][4 * h]);
                 }
             f32x4 be_[NT], eg_[NT];
 #pragma unroll
@@ -532,7 +543,8 @@ __global__ __launch_bounds__((NS + kPrepWaves) * 64) void gdn_fwd_pipe_kernel(Fw
                 split4(Vp[b], vph[b], vpl[b]);
             }
             if (c + 1 < nchunks) load_v(c + 1);
-            // ---- O^T = diag(exp g) Z^T + V'^T P^T (lane: row 16 rt + n, 4 columns) ----
+            __syncthreads();
+            // ---- phase B: O^T = diag(exp g) Z^T + V'^T P^T (lane: row 16 rt + n, 4 columns) ----
             f32x4 PVt[NT];
 #pragma unroll
             for (int rt = 0; rt < NT; ++rt) PVt[rt] = zero4();
