@@ -102,9 +102,12 @@ void launch_pipe(const gdn::FwdParams& p, long nblocks, hipStream_t st) {
 // Pipelined kernel: bf16 inputs, C in {32, 64}, d_k in {64, 128}.  NS scan
 // waves of 16 value columns each per workgroup: the largest of 4, 2, 1 that
 // divides d_v / 16 and still gives one workgroup per compute unit (256).
+// The pipelined kernel addresses one head's rows through 32-bit buffer
+// offsets, so one head's largest tensor (fp32 output) must stay below 2 GiB.
 bool pipe_supported(const gdn_shape& s) {
+    const size_t head_bytes = (size_t)s.T * (size_t)(s.d_k > s.d_v ? s.d_k : s.d_v) * 4;
     return s.qkv_dtype == GDN_BF16 && (s.chunk_size == 32 || s.chunk_size == 64) &&
-           (s.d_k == 64 || s.d_k == 128);
+           (s.d_k == 64 || s.d_k == 128) && head_bytes < ((size_t)1 << 31);
 }
 int choose_scan_waves(const gdn_shape& s) {
     const long heads = (long)s.B * s.H;

@@ -31,6 +31,32 @@ __device__ __forceinline__ f32x4 mfma_f32(float a, float b, f32x4 c) {
 
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
+// Raw buffer resource over [base, base + bytes), bytes < 2^31.  The hardware
+// range check of raw buffers makes loads at byte offsets >= bytes return zero
+// and drops stores there; offsets are per lane, 32-bit.
+typedef __amdgpu_buffer_rsrc_t buf_t;
+typedef __attribute__((ext_vector_type(2))) unsigned u32x2;
+typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
+__device__ __forceinline__ buf_t buffer_over(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+// one bf16 as its raw bits in the low half of a 32-bit register (kept
+// unpacked so that nothing waits for the load until the value is used)
+__device__ __forceinline__ uint32_t buf_load_bf16_bits(buf_t r, uint32_t off) {
+    return (uint32_t)(unsigned short)__builtin_amdgcn_raw_buffer_load_b16(r, (int)off, 0, 0);
+}
+__device__ __forceinline__ float bf16_bits_to_float(uint32_t b) { return __builtin_bit_cast(float, b << 16); }
+__device__ __forceinline__ uint4 buf_load_16B(buf_t r, uint32_t off) {
+    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+    return make_uint4(v[0], v[1], v[2], v[3]);
+}
+__device__ __forceinline__ void buf_store(buf_t r, uint32_t off, f32x4 v) {
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, (int)off, 0, 0);
+}
+__device__ __forceinline__ void buf_store(buf_t r, uint32_t off, bf16x4 v) {
+    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, v), r, (int)off, 0, 0);
+}
+
 // Round to bf16 (nearest-even) and the exact fp32 residual rounded again:
 // x ~= hi + lo with |x - hi - lo| <= 2^-17 |x| (about 16 significant bits).
 __device__ __forceinline__ void split_bf16(float x, __bf16& hi, __bf16& lo) {

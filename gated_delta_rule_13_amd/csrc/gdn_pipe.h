@@ -84,7 +84,7 @@ struct alignas(16) PipeLds {
     // block matrices by chunk parity: block (b, c<b) holds A_bc, block (b, b) holds T_bb
     __bf16 Bh[2][NB][16][16];           // hi
     __bf16 Bl[2][NB][16][16];           // lo
-    float Adt[NT][16][16];              // diagonal blocks of A, fp32, transposed: [b][k][i] = A_b[i][k]
+    float Ad[NT][16][16];               // diagonal blocks of A, fp32
     float g2[2][C];                     // inclusive cumsum of log2 alpha
     float er[2][C];                     // 2^(g2_r - g2_ref): row factor of exp(g_r - g_i)
     float fi[2][C];                     // 2^(g2_ref - g2_i): column factor
@@ -201,6 +201,9 @@ __global__ __launch_bounds__((NS + kPrepWaves) * 64) void gdn_fwd_pipe_kernel(Fw
     const __bf16* vb = reinterpret_cast<const __bf16*>(p.v) + (size_t)bh * T * dv;
     const float* ab = p.alpha ? p.alpha + (size_t)bh * T : nullptr;
     const float* bb = p.beta + (size_t)bh * T;
+    // per-head buffers: rows past the end of the sequence read as zero
+    const buf_t kbuf = buffer_over(kb, (uint32_t)T * DK * 2);
+    const buf_t qbuf = buffer_over(qb, (uint32_t)T * DK * 2);
     const int col0 = tile * DVT + 16 * wave;  // scan waves: first value column of this wave
 
     // the upper part of the score matrix stays zero
@@ -228,12 +231,12 @@ __global__ __launch_bounds__((NS + kPrepWaves) * 64) void gdn_fwd_pipe_kernel(Fw
                 constexpr int i = decltype(I)::value;
                 const int vi = plane + i * 64 * NP;
                 {
-                    const int r = min(vi % C, Lc - 1), c8 = (vi / C) * 8;
-                    stK[par][i] = *reinterpret_cast<const uint4*>(kb + (size_t)(t0 + r) * DK + c8);
+                    const int r = vi % C, c8 = (vi / C) * 8;
+                    stK[par][i] = buf_load_16B(kbuf, 2u * ((t0 + r) * DK + c8));
                 }
                 {
-                    const int r = min(vi / (DK / 8), Lc - 1), c8 = (vi % (DK / 8)) * 8;
-                    stQ[par][i] = *reinterpret_cast<const uint4*>(qb + (size_t)(t0 + r) * DK + c8);
+                    const int r = vi / (DK / 8), c8 = (vi % (DK / 8)) * 8;
+                    stQ[par][i] = buf_load_16B(qbuf, 2u * ((t0 + r) * DK + c8));
                 }
             });
             if (pw == 0) {
@@ -250,11 +253,9 @@ __global__ __launch_bounds__((NS + kPrepWaves) * 64) void gdn_fwd_pipe_kernel(Fw
                 constexpr int i = decltype(I)::value;
                 const int vi = plane + i * 64 * NP;
                 {
+                    // rows past the end of the sequence were loaded as zeros
                     const int r = vi % C, c8 = (vi / C) * 8;
-                    // rows past the end of the sequence are zeroed (value mask)
-                    const unsigned m = r < Lc ? 0xffffffffu : 0u;
-                    const uint4 sv = stK[par][i];
-                    const uint4 kv = make_uint4(sv.x & m, sv.y & m, sv.z & m, sv.w & m);
+                    const uint4 kv = stK[par][i];
                     *reinterpret_cast<uint4*>(&s.K[buf][r][c8]) = kv;
                     static_for<0, 8>([&](auto X) {
                         constexpr int x = decltype(X)::value;
@@ -265,10 +266,7 @@ __global__ __launch_bounds__((NS + kPrepWaves) * 64) void gdn_fwd_pipe_kernel(Fw
                 }
                 {
                     const int r = vi / (DK / 8), c8 = (vi % (DK / 8)) * 8;
-                    const unsigned m = r < Lc ? 0xffffffffu : 0u;
-                    const uint4 sv = stQ[par][i];
-                    *reinterpret_cast<uint4*>(&s.Q[buf][r][c8]) =
-                        make_uint4(sv.x & m, sv.y & m, sv.z & m, sv.w & m);
+                    *reinterpret_cast<uint4*>(&s.Q[buf][r][c8]) = stQ[par][i];
                 }
             });
             if (pw == 0) {
@@ -354,9 +352,8 @@ __global__ __launch_bounds__((NS + kPrepWaves) * 64) void gdn_fwd_pipe_kernel(Fw
                     *reinterpret_cast<bf16x4*>(&s.Ph[r][i0]) = hi;
                     *reinterpret_cast<bf16x4*>(&s.Pl[r][i0]) = lo;
                 } else if constexpr (kind == 0) {
-                    // element (row n, column 4h + e) of diagonal block rt, transposed
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) s.Adt[rt][4 * h + e][n] = v[e];
+                    // row n, columns 4h .. 4h + 3 of diagonal block rt
+                    *reinterpret_cast<f32x4*>(&s.Ad[rt][n][4 * h]) = v;
                 } else {
                     bf16x4 hi, lo;
                     split4(v, hi, lo);
@@ -366,36 +363,53 @@ __global__ __launch_bounds__((NS + kPrepWaves) * 64) void gdn_fwd_pipe_kernel(Fw
                 }
             });
         };
-        // T_bb = (I - A_bb)^{-1}, all diagonal blocks at once: lane (b, jj)
-        // runs forward substitution down column jj of block b, right-looking:
-        // once T[k][jj] is final it is added into every later row's partial
-        // sum, so only one multiply-add per row sits on the dependency chain.
+        // T_bb = (I - A_bb)^{-1}, all diagonal blocks at once: lane (b, i)
+        // computes row i of T_bb from T = I + T A, i.e. the transposed
+        // unit triangular system, by substitution from the last column down:
+        //     T[i][k] = [i == k] + sum_{m > k} T[i][m] A[m][k].
+        // Right-looking: once T[i][m] is final it is added into every
+        // earlier column's partial sum, so one multiply-add per step sits on
+        // the dependency chain.  Rows of A are read as broadcasts (lanes of
+        // one block read the same words), two steps ahead of their use.
         auto diag_solve = [&](int cc) __attribute__((always_inline)) {
             const int buf = cc & 1;
             if (lane < 16 * NT) {
-                const int b = lane >> 4, jj = lane & 15;
+                const int b = lane >> 4, i = lane & 15;
                 float part[16];
 #pragma unroll
-                for (int i = 0; i < 16; ++i) part[i] = 0.f;
-                float t[16];
+                for (int k = 0; k < 16; ++k) part[k] = (k == i) ? 1.f : 0.f;
+                float x[16];
+                f32x4 abuf[3][4];
+                auto load_row = [&](auto M) __attribute__((always_inline)) {
+                    constexpr int m = decltype(M)::value;
 #pragma unroll
-                for (int k = 0; k < 16; ++k) {
-                    t[k] = part[k] + ((k == jj) ? 1.f : 0.f);
+                    for (int q = 0; 4 * q < m; ++q)
+                        abuf[m % 3][q] = *reinterpret_cast<const f32x4*>(&s.Ad[b][m][4 * q]);
+                };
+                load_row(std::integral_constant<int, 15>{});
+                load_row(std::integral_constant<int, 14>{});
+                static_for<0, 16>([&](auto J) {
+                    constexpr int m = 15 - decltype(J)::value;
+                    if constexpr (m - 2 > 0) load_row(std::integral_constant<int, m - 2>{});
+                    x[m] = part[m];
 #pragma unroll
-                    for (int q = (k + 1) / 4; q < 4; ++q) {
-                        const f32x4 a = *reinterpret_cast<const f32x4*>(&s.Adt[b][k][4 * q]);
+                    for (int q = 0; 4 * q < m; ++q) {
+                        const f32x4 a = abuf[m % 3][q];
 #pragma unroll
                         for (int e = 0; e < 4; ++e)
-                            if (4 * q + e > k) part[4 * q + e] = fmaf(a[e], t[k], part[4 * q + e]);
+                            if (4 * q + e < m) part[4 * q + e] = fmaf(x[m], a[e], part[4 * q + e]);
                     }
-                }
+                });
+                bf16x4 hi[4], lo[4];
 #pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    __bf16 hi, lo;
-                    split_bf16(t[i], hi, lo);
-                    s.Bh[buf][L::bidx(b, b)][i][jj] = hi;
-                    s.Bl[buf][L::bidx(b, b)][i][jj] = lo;
-                }
+                for (int q = 0; q < 4; ++q)
+                    split4(f32x4{x[4 * q], x[4 * q + 1], x[4 * q + 2], x[4 * q + 3]}, hi[q], lo[q]);
+                __bf16* th = &s.Bh[buf][L::bidx(b, b)][i][0];
+                __bf16* tl = &s.Bl[buf][L::bidx(b, b)][i][0];
+                *reinterpret_cast<bf16x8*>(th) = __builtin_shufflevector(hi[0], hi[1], 0, 1, 2, 3, 4, 5, 6, 7);
+                *reinterpret_cast<bf16x8*>(th + 8) = __builtin_shufflevector(hi[2], hi[3], 0, 1, 2, 3, 4, 5, 6, 7);
+                *reinterpret_cast<bf16x8*>(tl) = __builtin_shufflevector(lo[0], lo[1], 0, 1, 2, 3, 4, 5, 6, 7);
+                *reinterpret_cast<bf16x8*>(tl + 8) = __builtin_shufflevector(lo[2], lo[3], 0, 1, 2, 3, 4, 5, 6, 7);
             }
         };
         // The whole prep loop is specialised per prep wave so that every tile
@@ -450,18 +464,22 @@ __global__ __launch_bounds__((NS + kPrepWaves) * 64) void gdn_fwd_pipe_kernel(Fw
     } else {
         // ============================ scan waves ============================
         f32x4 Sacc[NK];           // Sacc[t][j] = S[col0 + n][16 t + 4 h + j]
-        __bf16 vnext[NT][4];      // this lane's values of the next chunk, raw (zeroed at use)
+        uint32_t vnext[NT][4];    // this lane's values of the next chunk, bf16 bits (zero past the end)
+        const buf_t vbuf = buffer_over(vb, (uint32_t)T * dv * 2);
+        const uint32_t vlane = 2u * (4 * h * dv + col0 + n);
         auto load_v = [&](int cc) __attribute__((always_inline)) {
-            const int t0 = cc * C, Lc = min(C, T - t0);
+            const int t0 = cc * C;
             static_for<0, NT>([&](auto RT) {
                 constexpr int rt = decltype(RT)::value;
                 static_for<0, 4>([&](auto JJ) {
                     constexpr int j = decltype(JJ)::value;
-                    const int r = min(16 * rt + 4 * h + j, Lc - 1);
-                    vnext[rt][j] = vb[(size_t)(t0 + r) * dv + col0 + n];
+                    vnext[rt][j] = buf_load_bf16_bits(vbuf, vlane + 2u * (t0 + 16 * rt + j) * dv);
                 });
             });
         };
+        const int osz = p.o_bf16 ? 2 : 4;
+        const buf_t obuf = buffer_over(reinterpret_cast<const char*>(p.O) + (size_t)bh * T * dv * osz,
+                                       (uint32_t)T * dv * osz);
         const size_t sb = (size_t)bh * dv * DK + (size_t)(col0 + n) * DK;
 #pragma unroll
         for (int t = 0; t < NK; ++t)
@@ -473,7 +491,6 @@ __global__ __launch_bounds__((NS + kPrepWaves) * 64) void gdn_fwd_pipe_kernel(Fw
         for (int c = 0; c < nchunks; ++c) {
             const int buf = c & 1;
             const int t0 = c * C;
-            const int Lc = min(C, T - t0);
             // ---- phase A: X = K S^T, Z^T = S Q^T ----
             f32x4 X[NT], Zt[NT];
 #pragma unroll
@@ -520,9 +537,7 @@ __global__ __launch_bounds__((NS + kPrepWaves) * 64) void gdn_fwd_pipe_kernel(Fw
                 f32x4 y;
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    const int r = 16 * b + 4 * h + j;
-                    const float vv = r < Lc ? (float)vnext[b][j] : 0.f;
-                    y[j] = be_[b][j] * (vv - eg_[b][j] * X[b][j]);
+                    y[j] = be_[b][j] * (bf16_bits_to_float(vnext[b][j]) - eg_[b][j] * X[b][j]);
                 }
                 f32x4 a1 = zero4(), a2 = zero4(), a3 = zero4();
 #pragma unroll
@@ -542,8 +557,9 @@ __global__ __launch_bounds__((NS + kPrepWaves) * 64) void gdn_fwd_pipe_kernel(Fw
                 Vp[b] = t1 + t2 + t3;
                 split4(Vp[b], vph[b], vpl[b]);
             }
-            if (c + 1 < nchunks) load_v(c + 1);
             __syncthreads();
+            // the next chunk's values, consumed by the next phase A
+            if (c + 1 < nchunks) load_v(c + 1);
             // ---- phase B: O^T = diag(exp g) Z^T + V'^T P^T (lane: row 16 rt + n, 4 columns) ----
             f32x4 PVt[NT];
 #pragma unroll
@@ -571,17 +587,13 @@ __global__ __launch_bounds__((NS + kPrepWaves) * 64) void gdn_fwd_pipe_kernel(Fw
             }
 #pragma unroll
             for (int rt = 0; rt < NT; ++rt) {
+                // rows past the end of the sequence fall outside the buffer (dropped)
                 const int r = 16 * rt + n;
-                if (r < Lc) {
-                    const float e = s.eg[buf][r];
-                    const f32x4 o = e * Zt[rt] + PVt[rt];
-                    const size_t off = ((size_t)bh * T + t0 + r) * dv + col0 + 4 * h;
-                    if (p.o_bf16)
-                        *reinterpret_cast<bf16x4*>(reinterpret_cast<__bf16*>(p.O) + off) =
-                            __builtin_convertvector(o, bf16x4);
-                    else
-                        *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(p.O) + off) = o;
-                }
+                const float e = s.eg[buf][r];
+                const f32x4 o = e * Zt[rt] + PVt[rt];
+                const uint32_t off = (uint32_t)((t0 + r) * dv + col0 + 4 * h) * osz;
+                if (p.o_bf16) buf_store(obuf, off, __builtin_convertvector(o, bf16x4));
+                else buf_store(obuf, off, o);
             }
             // ---- S^T <- exp(g_last) S^T + K^T diag(exp(g_last - g)) V' ----
             const float gl = s.glast[buf];
