@@ -73,7 +73,14 @@ template <int C, int DK>
 struct alignas(16) PipeLds {
     static constexpr int NT = C / 16;
     static constexpr int KP = DK + 8;   // row stride of key / query tiles (bf16)
-    static constexpr int CP = C + 8;    // row stride of C-wide rows (bf16)
+    // Row strides against LDS bank conflicts (32 banks of 4 bytes; an 8-byte
+    // access serves 16 lanes per pass): 8-byte column slices of 16
+    // consecutive rows hit distinct banks when the stride is an odd multiple
+    // of 8 bytes modulo 128, as for C + 4 bf16 (C = 32, 64) and 20 bf16;
+    // 16-byte slices of 8 rows when it is an odd multiple of 16, as for
+    // 20 floats.
+    static constexpr int CP = C + 4;    // row stride of C-wide rows (bf16)
+    static constexpr int BP = 20;       // row stride of 16 x 16 blocks (bf16 and fp32)
     __bf16 K[2][C][KP];
     __bf16 Q[2][C][KP];
     __bf16 Kt[2][DK][CP];
@@ -82,9 +89,9 @@ struct alignas(16) PipeLds {
     static constexpr int NB = NT * (NT + 1) / 2;   // blocks on and below the diagonal
     static constexpr int bidx(int b, int cb) { return b * (b + 1) / 2 + cb; }
     // block matrices by chunk parity: block (b, c<b) holds A_bc, block (b, b) holds T_bb
-    __bf16 Bh[2][NB][16][16];           // hi
-    __bf16 Bl[2][NB][16][16];           // lo
-    float Ad[NT][16][16];               // diagonal blocks of A, fp32
+    __bf16 Bh[2][NB][16][BP];           // hi
+    __bf16 Bl[2][NB][16][BP];           // lo
+    float Ad[NT][16][BP];               // diagonal blocks of A, fp32
     float g2[2][C];                     // inclusive cumsum of log2 alpha
     float er[2][C];                     // 2^(g2_r - g2_ref): row factor of exp(g_r - g_i)
     float fi[2][C];                     // 2^(g2_ref - g2_i): column factor
@@ -406,10 +413,11 @@ __global__ __launch_bounds__((NS + kPrepWaves) * 64) void gdn_fwd_pipe_kernel(Fw
                     split4(f32x4{x[4 * q], x[4 * q + 1], x[4 * q + 2], x[4 * q + 3]}, hi[q], lo[q]);
                 __bf16* th = &s.Bh[buf][L::bidx(b, b)][i][0];
                 __bf16* tl = &s.Bl[buf][L::bidx(b, b)][i][0];
-                *reinterpret_cast<bf16x8*>(th) = __builtin_shufflevector(hi[0], hi[1], 0, 1, 2, 3, 4, 5, 6, 7);
-                *reinterpret_cast<bf16x8*>(th + 8) = __builtin_shufflevector(hi[2], hi[3], 0, 1, 2, 3, 4, 5, 6, 7);
-                *reinterpret_cast<bf16x8*>(tl) = __builtin_shufflevector(lo[0], lo[1], 0, 1, 2, 3, 4, 5, 6, 7);
-                *reinterpret_cast<bf16x8*>(tl + 8) = __builtin_shufflevector(lo[2], lo[3], 0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    *reinterpret_cast<bf16x4*>(th + 4 * q) = hi[q];
+                    *reinterpret_cast<bf16x4*>(tl + 4 * q) = lo[q];
+                }
             }
         };
         // The whole prep loop is specialised per prep wave so that every tile
