@@ -69,16 +69,24 @@ __device__ __forceinline__ void static_for(F&& f) {
 
 constexpr int kPrepWaves = 4;
 
+// eight consecutive elements [32 s + 8 h, +8) of an 8-byte aligned row, as two 8-byte reads
+__device__ __forceinline__ bf16x8 ld_nat8_b64(const __bf16* row, int s, int h) {
+    const bf16x4 a = *reinterpret_cast<const bf16x4*>(row + 32 * s + 8 * h);
+    const bf16x4 b = *reinterpret_cast<const bf16x4*>(row + 32 * s + 8 * h + 4);
+    return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
 template <int C, int DK>
 struct alignas(16) PipeLds {
     static constexpr int NT = C / 16;
-    static constexpr int KP = DK + 8;   // row stride of key / query tiles (bf16)
+    static constexpr int KP = DK + 4;   // row stride of key / query tiles (bf16): 8-byte aligned rows
     // Row strides against LDS bank conflicts (32 banks of 4 bytes; an 8-byte
     // access serves 16 lanes per pass): 8-byte column slices of 16
     // consecutive rows hit distinct banks when the stride is an odd multiple
     // of 8 bytes modulo 128, as for C + 4 bf16 (C = 32, 64) and 20 bf16;
     // 16-byte slices of 8 rows when it is an odd multiple of 16, as for
-    // 20 floats.
+    // 20 floats.  Key / query rows (d_k + 4 bf16) are only 8-byte aligned,
+    // so they are written and read in 8-byte pieces.
     static constexpr int CP = C + 4;    // row stride of C-wide rows (bf16)
     static constexpr int BP = 20;       // row stride of 16 x 16 blocks (bf16 and fp32)
     __bf16 K[2][C][KP];
@@ -263,7 +271,8 @@ __global__ __launch_bounds__((NS + kPrepWaves) * 64) void gdn_fwd_pipe_kernel(Fw
                     // rows past the end of the sequence were loaded as zeros
                     const int r = vi % C, c8 = (vi / C) * 8;
                     const uint4 kv = stK[par][i];
-                    *reinterpret_cast<uint4*>(&s.K[buf][r][c8]) = kv;
+                    *reinterpret_cast<uint2*>(&s.K[buf][r][c8]) = make_uint2(kv.x, kv.y);
+                    *reinterpret_cast<uint2*>(&s.K[buf][r][c8 + 4]) = make_uint2(kv.z, kv.w);
                     static_for<0, 8>([&](auto X) {
                         constexpr int x = decltype(X)::value;
                         const unsigned word = x < 2 ? kv.x : x < 4 ? kv.y : x < 6 ? kv.z : kv.w;
@@ -273,7 +282,9 @@ __global__ __launch_bounds__((NS + kPrepWaves) * 64) void gdn_fwd_pipe_kernel(Fw
                 }
                 {
                     const int r = vi / (DK / 8), c8 = (vi % (DK / 8)) * 8;
-                    *reinterpret_cast<uint4*>(&s.Q[buf][r][c8]) = stQ[par][i];
+                    const uint4 qv = stQ[par][i];
+                    *reinterpret_cast<uint2*>(&s.Q[buf][r][c8]) = make_uint2(qv.x, qv.y);
+                    *reinterpret_cast<uint2*>(&s.Q[buf][r][c8 + 4]) = make_uint2(qv.z, qv.w);
                 }
             });
             if (pw == 0) {
@@ -315,7 +326,7 @@ __global__ __launch_bounds__((NS + kPrepWaves) * 64) void gdn_fwd_pipe_kernel(Fw
                 f32x4 acc = zero4();
 #pragma unroll
                 for (int ss = 0; ss < DK / 32; ++ss)
-                    acc = mfma_bf16(ld_nat8(arow, ss, h), ld_nat8(brow, ss, h), acc);
+                    acc = mfma_bf16(ld_nat8_b64(arow, ss, h), ld_nat8_b64(brow, ss, h), acc);
                 gacc[j] = acc;
             });
         };
