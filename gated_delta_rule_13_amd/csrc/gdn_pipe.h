@@ -12,7 +12,7 @@
 //    by blocks):
 //        V'_b = T_bb (diag(beta_b) Y_b + sum_{c<b} A_bc V'_c),
 //    where T_bb = (I - A_bb)^{-1} are the 16 x 16 diagonal blocks, solved by
-//    forward substitution on VALU (one lane per column).  The coupling terms
+//    substitution on VALU (one lane per row of T_bb).  The coupling terms
 //    A_bc V'_c are dense 16 x 16 x 16 contractions and run on MFMA.
 // 2. Work is split by role inside the workgroup: NS "scan" waves each own 16
 //    value columns and that slice of the fp32 state (S^T in MFMA
