@@ -5,7 +5,9 @@
 A step is one gdn_chunk_fwd call (the whole hot path: decay prefix, Gram and
 scores, triangular solve, pseudo-values, output and state scan, all in one
 kernel) over the workload's seeded synthetic inputs, already resident in HBM.
-Prints one JSON line.  ``value`` is tokens/s = B * T / seconds per step.
+For the ``decode`` workload a step is one gdn_recurrent_fwd call (one token
+per sequence against a resident state).  Prints one JSON line.  ``value`` is
+tokens/s = B * T / seconds per step.
 
 roofline: the fused kernel's algorithmic bytes (read q, k, v, alpha, beta,
 S0 once; write O and S_final once) divided by its mean duration, measured with
@@ -30,6 +32,7 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0      # dense bf16 MFMA
 METRIC = "tokens/s and achieved TFLOP/s (% roofline), GDN fwd H=16 T=4096 d=128, 1 MI355X"
 KERNEL_SOURCES = ["gated_delta_rule_13_amd/csrc/gdn_pipe.h",
+                  "gated_delta_rule_13_amd/csrc/gdn_recurrent.h",
                   "gated_delta_rule_13_amd/csrc/gdn_kernels.h",
                   "gated_delta_rule_13_amd/csrc/gdn_device.h",
                   "gated_delta_rule_13_amd/csrc/gdn_api.hip"]
@@ -132,9 +135,15 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
 
+    recurrent = w.name == "decode"
+
     def step():
-        gdn.gdn_chunk_fwd(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["S0"],
-                          chunk_size=w.chunk, o_dtype=o_dtype, O=O, S_final=S)
+        if recurrent:
+            gdn.gdn_recurrent_fwd(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["S0"],
+                                  o_dtype=o_dtype, O=O, S_final=S)
+        else:
+            gdn.gdn_chunk_fwd(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["S0"],
+                              chunk_size=w.chunk, o_dtype=o_dtype, O=O, S_final=S)
 
     for _ in range(args.warmup):
         step()
@@ -178,7 +187,9 @@ def main():
         "dtype": "bf16" if w.dtype == "bf16" else "f32",
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "T": w.T, "d_k": w.dk, "d_v": w.dv,
-                   "chunk": w.chunk, "o_dtype": args.o_dtype, "parallelism": "none (1 GPU)"},
+                   "chunk": None if recurrent else w.chunk, "o_dtype": args.o_dtype,
+                   "path": "recurrent" if recurrent else "chunked",
+                   "parallelism": "none (1 GPU)"},
         "head_tokens_per_s": tokens * w.H / (wall / args.steps),
         "tflops": alg_flops / (wall / args.steps) / 1e12,
         "kernel_ms": {"mean": mean_kern_s * 1e3, "p10": kern_ms[len(kern_ms) // 10],
@@ -186,7 +197,8 @@ def main():
         "roofline": {"bound": "hbm", "achieved": achieved_gbs, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved_gbs / HBM_PEAK_GBS, "traffic": traffic,
                      "algorithmic_bytes": alg_bytes,
-                     "mfma_frac": alg_flops / mean_kern_s / 1e12 / BF16_PEAK_TFLOPS},
+                     "mfma_frac": None if recurrent else
+                     alg_flops / mean_kern_s / 1e12 / BF16_PEAK_TFLOPS},
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

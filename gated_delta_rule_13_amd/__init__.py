@@ -15,7 +15,7 @@ import ctypes
 
 from ._lib import (EXPORTS, GDN_BF16, GDN_F32, GdnError, GdnShape, check, load)
 
-__all__ = ["gdn_chunk_fwd", "gdn_chunk_prep", "gdn_chunk_fwd_workspace_bytes",
+__all__ = ["gdn_chunk_fwd", "gdn_chunk_prep", "gdn_chunk_fwd_workspace_bytes", "gdn_recurrent_fwd",
            "gdn_status_string", "gdn_last_error", "gdn_version", "GdnError", "GdnShape",
            "EXPORTS"]
 
@@ -104,6 +104,39 @@ def gdn_chunk_fwd(q, k, v, alpha, beta, S0=None, chunk_size: int = 64, o_dtype=N
     st = lib.gdn_chunk_fwd(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha),
                            _ptr(beta), _ptr(S0), _ptr(O), _ptr(S_final), _ptr(ws), ws_bytes,
                            _stream_handle(dev, stream))
+    check(st)
+    return O, S_final
+
+
+def gdn_recurrent_fwd(q, k, v, alpha, beta, S0=None, o_dtype=None, O=None, S_final=None,
+                      stream=None):
+    """Token-by-token forward pass on the GPU (short T, e.g. a decode step).
+    Same tensors and conventions as gdn_chunk_fwd; S_final may be S0 (the
+    state is then updated in place)."""
+    torch = _torch()
+    lib = load()
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("gdn_recurrent_fwd runs on the GPU: tensors must be on a cuda device")
+    o_dtype = torch.float32 if o_dtype is None else o_dtype
+    _check_tensor("q", q, (B, H, T, dk), q.dtype, dev)
+    _check_tensor("k", k, (B, H, T, dk), q.dtype, dev)
+    _check_tensor("v", v, (B, H, T, dv), q.dtype, dev)
+    _check_tensor("alpha", alpha, (B, H, T), torch.float32, dev)
+    _check_tensor("beta", beta, (B, H, T), torch.float32, dev)
+    _check_tensor("S0", S0, (B, H, dv, dk), torch.float32, dev)
+    if O is None:
+        O = torch.empty((B, H, T, dv), dtype=o_dtype, device=dev)
+    _check_tensor("O", O, (B, H, T, dv), o_dtype, dev)
+    if S_final is None:
+        S_final = torch.empty((B, H, dv, dk), dtype=torch.float32, device=dev)
+    _check_tensor("S_final", S_final, (B, H, dv, dk), torch.float32, dev)
+    shape = make_shape(B, H, T, dk, dv, 1, q.dtype, o_dtype)
+    st = lib.gdn_recurrent_fwd(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha),
+                               _ptr(beta), _ptr(S0), _ptr(O), _ptr(S_final),
+                               _stream_handle(dev, stream))
     check(st)
     return O, S_final
 

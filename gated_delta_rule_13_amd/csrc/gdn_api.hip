@@ -9,6 +9,7 @@
 #include "gdn.h"
 #include "gdn_kernels.h"
 #include "gdn_pipe.h"
+#include "gdn_recurrent.h"
 
 namespace {
 
@@ -162,6 +163,31 @@ Launcher pick(const gdn_shape& s, int nw, bool prep) {
     return nullptr;
 }
 
+using RecLauncher = void (*)(const gdn::RecParams&, long, hipStream_t);
+
+template <int DK, bool BF>
+void launch_rec(const gdn::RecParams& p, long nblocks, hipStream_t st) {
+    hipLaunchKernelGGL((gdn::gdn_recurrent_kernel<DK, BF>), dim3((unsigned)nblocks),
+                       dim3(gdn::kRecThreads), 0, st, p);
+}
+
+RecLauncher pick_rec(int dk, bool bf, int* rows_per_block) {
+#define GDN_REC(D)                                                               \
+    if (dk == D) {                                                               \
+        *rows_per_block = (gdn::kRecThreads / 64) * (64 / gdn::rec_lanes_per_row(D)); \
+        return bf ? launch_rec<D, true> : launch_rec<D, false>;                  \
+    }
+    GDN_REC(16)
+    GDN_REC(32)
+    GDN_REC(64)
+    GDN_REC(96)
+    GDN_REC(128)
+    GDN_REC(192)
+    GDN_REC(256)
+#undef GDN_REC
+    return nullptr;
+}
+
 gdn_status check_launch() {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(GDN_ERR_HIP, hipGetErrorString(e));
@@ -246,6 +272,46 @@ gdn_status gdn_chunk_prep(const gdn_shape* s, const void* k, const void* v, cons
     p.n_tiles = s->d_v / (16 * nw);
     const long nchunks = (s->T + s->chunk_size - 1) / s->chunk_size;
     const long nblocks = (long)s->B * s->H * nchunks * p.n_tiles;
+    if (nblocks > 0x7fffffffL) return fail(GDN_ERR_BAD_SHAPE, "grid too large");
+    launch(p, nblocks, reinterpret_cast<hipStream_t>(stream));
+    return check_launch();
+}
+
+gdn_status gdn_recurrent_fwd(const gdn_shape* s, const void* q, const void* k, const void* v,
+                             const float* alpha, const float* beta, const float* S0, void* O,
+                             float* S_final, void* stream) {
+    g_last_error.clear();
+    if (!s) return fail(GDN_ERR_NULL_ARG, "shape is NULL");
+    if (s->B < 1 || s->H < 1 || s->T < 1 || s->d_k < 1 || s->d_v < 1)
+        return fail(GDN_ERR_BAD_SHAPE, "B, H, T, d_k and d_v must be >= 1");
+    if ((s->qkv_dtype != GDN_BF16 && s->qkv_dtype != GDN_F32) ||
+        (s->o_dtype != GDN_BF16 && s->o_dtype != GDN_F32))
+        return fail(GDN_ERR_BAD_DTYPE, "dtype must be GDN_BF16 or GDN_F32");
+    const long double elems = (long double)s->B * s->H * s->T * (s->d_k > s->d_v ? s->d_k : s->d_v);
+    if (elems > 4.0e18L) return fail(GDN_ERR_BAD_SHAPE, "tensor too large");
+    if (s->d_v > 65536) return fail(GDN_ERR_UNSUPPORTED, "d_v must be <= 65536");
+    int rpb = 0;
+    const RecLauncher launch = pick_rec(s->d_k, s->qkv_dtype == GDN_BF16, &rpb);
+    if (!launch) return fail(GDN_ERR_UNSUPPORTED, "d_k must be one of 16, 32, 64, 96, 128, 192, 256");
+    if (!q || !k || !v || !beta || !O || !S_final)
+        return fail(GDN_ERR_NULL_ARG, "q, k, v, beta, O and S_final are required");
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(O) || !aligned16(S_final) ||
+        (S0 && !aligned16(S0)) || !aligned16(beta) || (alpha && !aligned16(alpha)))
+        return fail(GDN_ERR_UNSUPPORTED, "tensor pointers must be 16-byte aligned");
+    gdn::RecParams p{};
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.alpha = alpha;
+    p.beta = beta;
+    p.S0 = S0;
+    p.O = O;
+    p.S_final = S_final;
+    p.T = s->T;
+    p.dv = s->d_v;
+    p.blocks_per_head = (s->d_v + rpb - 1) / rpb;
+    p.o_bf16 = s->o_dtype == GDN_BF16;
+    const long nblocks = (long)s->B * s->H * p.blocks_per_head;
     if (nblocks > 0x7fffffffL) return fail(GDN_ERR_BAD_SHAPE, "grid too large");
     launch(p, nblocks, reinterpret_cast<hipStream_t>(stream));
     return check_launch();

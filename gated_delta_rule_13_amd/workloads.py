@@ -4,7 +4,7 @@ This module holds input generation only -- none of the method's arithmetic --
 so that the GPU path and the CPU oracle can both be fed from it without
 sharing any code with each other.
 
-Five workloads, named by what they are.  All draws come from one CPU
+Six workloads, named by what they are.  All draws come from one CPU
 ``torch.Generator`` seeded with ``seed``, in the fixed order
 q, k, v, S0, beta source, alpha source, reflection mask; each is drawn in
 float32 with the full shape.  q and k are L2-normalised per row in float32
@@ -20,6 +20,8 @@ main           4, 16, 4096, 128, 128, 64                   bf16    beta = sigmoi
 long           1, 32, 32768, 128, 256, 64                  bf16    beta = sigmoid(N), alpha = exp(-softplus(N) * 0.01), S0 = 0.02 N
 many_short     64, 8, 512, 128, 128, 32                    bf16    beta ~ U(0,1), alpha ~ U(0.9,1); 1% of tokens (Bernoulli per token)
                                                                    are reflections: beta = 2 / (k^T k), alpha = 1; S0 = 0
+decode         64, 16, 1, 128, 128, -                      bf16    beta = sigmoid(N), alpha = exp(-softplus(N) * 0.05),
+                                                                   S0 = 0.02 N: one decode step of the recurrent form
 =============  ==========================================  ======  ============================
 
 v ~ N(0, 1) everywhere.  Alpha of exactly one is passed as ``None`` (the
@@ -69,6 +71,10 @@ WORKLOADS = {
                      s0_std=0.02),
     "many_short": Workload("many_short", 64, 8, 512, 128, 128, 32, "bf16",
                            beta_kind="uniform", alpha_kind="uniform", reflection_rate=0.01),
+    # one token per sequence against a resident state (recurrent form; the
+    # chunk field is unused there)
+    "decode": Workload("decode", 64, 16, 1, 128, 128, 64, "bf16", alpha_scale=0.05,
+                       s0_std=0.02),
 }
 
 _TORCH_DTYPE = {"bf16": torch.bfloat16, "f32": torch.float32}

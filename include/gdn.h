@@ -119,6 +119,29 @@ gdn_status gdn_chunk_prep(const gdn_shape* s,
                           void* workspace, size_t workspace_bytes,
                           void* stream);
 
+/*
+ * Recurrent (token-by-token) forward pass: the same recurrence applied one
+ * token at a time ("从零开始的 GDN 推导", recurrent form; "RNN的复兴03",
+ * section 1), for short sequences such as a decode step appended to a
+ * chunked prefill.  The state is read once, kept on chip for all T tokens
+ * and written once, so for T = 1 the cost is one pass of the state through
+ * HBM.  Same tensors, layouts and conventions as gdn_chunk_fwd:
+ *   q, k [B, H, T, d_k], v [B, H, T, d_v] (qkv_dtype), alpha (NULL = 1) and
+ *   beta [B, H, T] float, S0 [B, H, d_v, d_k] float (NULL = zero),
+ *   O [B, H, T, d_v] (o_dtype), S_final [B, H, d_v, d_k] float; S_final may
+ *   be the same pointer as S0 (in-place update), other overlaps are not
+ *   allowed.  chunk_size is ignored.
+ * Supported: qkv_dtype GDN_BF16 or GDN_F32; d_k in {16, 32, 64, 96, 128,
+ * 192, 256}; 1 <= d_v <= 65536; any T >= 1 (the work is serial in T, so long
+ * sequences belong to gdn_chunk_fwd).  Pointers 16-byte aligned.  Errors are
+ * returned before any launch, as for gdn_chunk_fwd.
+ */
+gdn_status gdn_recurrent_fwd(const gdn_shape* s,
+                             const void* q, const void* k, const void* v,
+                             const float* alpha, const float* beta, const float* S0,
+                             void* O, float* S_final,
+                             void* stream);
+
 /* Static text for a status code. */
 const char* gdn_status_string(gdn_status st);
 

@@ -117,3 +117,28 @@ def test_binding_rejects_cpu_tensors():
     b = torch.zeros(1, 1, 4)
     with pytest.raises(ValueError, match="GPU"):
         gdn.gdn_chunk_fwd(x, x, x, None, b)
+
+
+def rec(lib, s, **ptrs):
+    p = dict(q=FAKE, k=FAKE, v=FAKE, alpha=None, beta=FAKE, S0=None, O=FAKE, S=FAKE)
+    p.update(ptrs)
+    sp = ctypes.byref(s) if s is not None else None
+    return lib.gdn_recurrent_fwd(sp, p["q"], p["k"], p["v"], p["alpha"], p["beta"], p["S0"],
+                                 p["O"], p["S"], None)
+
+
+@pytest.mark.parametrize("kw,expected", [
+    (dict(B=0), 2), (dict(T=0), 2), (dict(d_v=0), 2), (dict(qkv_dtype=5), 3),
+    (dict(d_k=48), 4), (dict(d_k=512), 4), (dict(d_v=70000), 4),
+])
+def test_recurrent_bad_shapes_rejected(lib, kw, expected):
+    assert rec(lib, shape(**kw)) == expected
+    assert lib.gdn_last_error().decode() != ""
+
+
+def test_recurrent_null_and_misaligned_rejected(lib):
+    assert rec(lib, None) == 1
+    for name in ("q", "k", "v", "beta", "O", "S"):
+        assert rec(lib, shape(), **{name: None}) == 1, name
+    for name in ("q", "k", "v", "beta", "O", "S", "alpha", "S0"):
+        assert rec(lib, shape(), **{name: ctypes.c_void_p(0x10004)}) == 4, name
