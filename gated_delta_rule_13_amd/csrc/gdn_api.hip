@@ -174,7 +174,7 @@ void launch_rec(const gdn::RecParams& p, long nblocks, hipStream_t st) {
 RecLauncher pick_rec(int dk, bool bf, int* rows_per_block) {
 #define GDN_REC(D)                                                               \
     if (dk == D) {                                                               \
-        *rows_per_block = (gdn::kRecThreads / 64) * (64 / gdn::rec_lanes_per_row(D)); \
+        *rows_per_block = gdn::kRecRows * (gdn::kRecThreads / 64) * (64 / gdn::rec_lanes_per_row(D)); \
         return bf ? launch_rec<D, true> : launch_rec<D, false>;                  \
     }
     GDN_REC(16)

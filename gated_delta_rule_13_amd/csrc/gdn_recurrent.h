@@ -32,37 +32,62 @@ struct RecParams {
     int o_bf16;
 };
 
-// Lanes per state row: the largest power of two <= 32 with d_k = 4 * LPR * J.
-constexpr int rec_lanes_per_row(int dk) {
-    int l = 32;
-    while (l > 1 && dk % (4 * l) != 0) l /= 2;
-    return l;
+// Lanes per state row: 8 (4 when d_k = 16), so that a row's sum over its
+// lanes is three DPP steps within a row of 16 lanes, and each lane streams
+// d_k / 32 16-byte pieces of its row (many bytes in flight per wave).
+constexpr int rec_lanes_per_row(int dk) { return dk % 32 == 0 ? 8 : 4; }
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xf, 0xf, false));
+}
+
+// Sum over aligned groups of LPR (4 or 8) lanes, result in every lane:
+// quad_perm [1,0,3,2] and [2,3,0,1] sum each quad of lanes, then
+// row_half_mirror (lane i <-> 7 - i within 8 lanes) adds the other quad.
+template <int LPR>
+__device__ __forceinline__ float group_sum(float x) {
+    x += dpp_f32<0xB1>(x);
+    x += dpp_f32<0x4E>(x);
+    if constexpr (LPR == 8) x += dpp_f32<0x141>(x);
+    return x;
 }
 
 constexpr int kRecThreads = 256;
+
+// Rows per lane group: each group keeps R rows (RPB / R apart), so k_t and
+// q_t are loaded once per token for R rows and R times the state bytes are
+// in flight per lane.
+constexpr int kRecRows = 4;
 
 template <int DK, bool BF>
 __global__ __launch_bounds__(kRecThreads) void gdn_recurrent_kernel(RecParams p) {
     constexpr int LPR = rec_lanes_per_row(DK);
     constexpr int J = DK / (4 * LPR);
-    constexpr int RPW = 64 / LPR;                     // rows per wave
-    constexpr int RPB = (kRecThreads / 64) * RPW;     // rows per workgroup
+    constexpr int R = kRecRows;
+    constexpr int RPW = 64 / LPR;                     // row groups per wave
+    constexpr int GPB = (kRecThreads / 64) * RPW;     // row groups per workgroup
     static_assert(DK == 4 * LPR * J, "d_k must be a multiple of 4");
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int m = lane % LPR;
     const long bh = blockIdx.x / p.blocks_per_head;
-    const int row = (blockIdx.x % p.blocks_per_head) * RPB + wave * RPW + lane / LPR;
-    const bool valid = row < p.dv;   // uniform over a row's lane group
+    const int row0 = (blockIdx.x % p.blocks_per_head) * GPB * R + wave * RPW + lane / LPR;
     const int T = p.T, dv = p.dv;
 
-    f32x4 S[J];
-    const size_t srow = ((size_t)bh * dv + row) * DK;
+    // rows row0 + GPB * r, r < R; validity is uniform over a lane group
+    f32x4 S[R][J];
 #pragma unroll
-    for (int j = 0; j < J; ++j)
-        S[j] = (valid && p.S0) ? *reinterpret_cast<const f32x4*>(p.S0 + srow + 4 * m + 4 * LPR * j)
-                               : zero4();
+    for (int r = 0; r < R; ++r) {
+        const int row = row0 + GPB * r;
+        const size_t srow = ((size_t)bh * dv + row) * DK;
+#pragma unroll
+        for (int j = 0; j < J; ++j)
+            S[r][j] = (row < dv && p.S0)
+                          ? *reinterpret_cast<const f32x4*>(p.S0 + srow + 4 * m + 4 * LPR * j)
+                          : zero4();
+    }
 
     for (int t = 0; t < T; ++t) {
         const size_t tok = (size_t)bh * T + t;
@@ -82,40 +107,48 @@ __global__ __launch_bounds__(kRecThreads) void gdn_recurrent_kernel(RecParams p)
         }
         const float a = p.alpha ? p.alpha[tok] : 1.f;
         const float b = p.beta[tok];
-        float vv = 0.f;
-        if (valid) {
-            vv = BF ? (float)reinterpret_cast<const __bf16*>(p.v)[tok * dv + row]
-                    : reinterpret_cast<const float*>(p.v)[tok * dv + row];
-        }
-        // u = S_{t-1} k_t over the row
-        float u = 0.f;
 #pragma unroll
-        for (int j = 0; j < J; ++j)
+        for (int r = 0; r < R; ++r) {
+            const int row = row0 + GPB * r;
+            const bool valid = row < dv;
+            float vv = 0.f;
+            if (valid) {
+                vv = BF ? (float)reinterpret_cast<const __bf16*>(p.v)[tok * dv + row]
+                        : reinterpret_cast<const float*>(p.v)[tok * dv + row];
+            }
+            // u = S_{t-1} k_t over the row
+            float u = 0.f;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) u = fmaf(S[j][e], kk[j][e], u);
+            for (int j = 0; j < J; ++j)
 #pragma unroll
-        for (int o = LPR / 2; o > 0; o >>= 1) u += __shfl_xor(u, o, 64);
-        const float coef = b * (vv - a * u);
-        float ot = 0.f;
+                for (int e = 0; e < 4; ++e) u = fmaf(S[r][j][e], kk[j][e], u);
+            u = group_sum<LPR>(u);
+            const float coef = b * (vv - a * u);
+            float ot = 0.f;
 #pragma unroll
-        for (int j = 0; j < J; ++j) {
+            for (int j = 0; j < J; ++j) {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                S[j][e] = fmaf(coef, kk[j][e], a * S[j][e]);
-                ot = fmaf(S[j][e], qq[j][e], ot);
+                for (int e = 0; e < 4; ++e) {
+                    S[r][j][e] = fmaf(coef, kk[j][e], a * S[r][j][e]);
+                    ot = fmaf(S[r][j][e], qq[j][e], ot);
+                }
+            }
+            ot = group_sum<LPR>(ot);
+            if (valid && m == 0) {
+                if (p.o_bf16) reinterpret_cast<__bf16*>(p.O)[tok * dv + row] = (__bf16)ot;
+                else reinterpret_cast<float*>(p.O)[tok * dv + row] = ot;
             }
         }
-#pragma unroll
-        for (int o = LPR / 2; o > 0; o >>= 1) ot += __shfl_xor(ot, o, 64);
-        if (valid && m == 0) {
-            if (p.o_bf16) reinterpret_cast<__bf16*>(p.O)[tok * dv + row] = (__bf16)ot;
-            else reinterpret_cast<float*>(p.O)[tok * dv + row] = ot;
-        }
     }
-    if (valid) {
 #pragma unroll
-        for (int j = 0; j < J; ++j)
-            *reinterpret_cast<f32x4*>(p.S_final + srow + 4 * m + 4 * LPR * j) = S[j];
+    for (int r = 0; r < R; ++r) {
+        const int row = row0 + GPB * r;
+        if (row < dv) {
+            const size_t srow = ((size_t)bh * dv + row) * DK;
+#pragma unroll
+            for (int j = 0; j < J; ++j)
+                *reinterpret_cast<f32x4*>(p.S_final + srow + 4 * m + 4 * LPR * j) = S[r][j];
+        }
     }
 }
 
