@@ -15,7 +15,8 @@ import ctypes
 
 from ._lib import (EXPORTS, GDN_BF16, GDN_F32, GdnError, GdnShape, check, load)
 
-__all__ = ["gdn_chunk_fwd", "gdn_chunk_prep", "gdn_chunk_fwd_workspace_bytes", "gdn_recurrent_fwd",
+__all__ = ["gdn_chunk_fwd", "gdn_chunk_fwd_eta", "gdn_chunk_prep", "gdn_chunk_fwd_workspace_bytes",
+           "gdn_recurrent_fwd", "gdn_recurrent_fwd_eta",
            "gdn_status_string", "gdn_last_error", "gdn_version", "GdnError", "GdnShape",
            "EXPORTS"]
 
@@ -72,12 +73,14 @@ def gdn_chunk_fwd_workspace_bytes(shape: GdnShape) -> int:
 
 
 def gdn_chunk_fwd(q, k, v, alpha, beta, S0=None, chunk_size: int = 64, o_dtype=None,
-                  O=None, S_final=None, stream=None):
+                  O=None, S_final=None, stream=None, eta=None):
     """Forward pass on the GPU.  q, k [B,H,T,d_k] and v [B,H,T,d_v] (bf16 or
     fp32, one dtype); alpha (or None = 1), beta [B,H,T] fp32; S0 [B,H,d_v,d_k]
     fp32 or None (zero).  Returns (O [B,H,T,d_v] in o_dtype (fp32 default),
     S_final [B,H,d_v,d_k] fp32).  O / S_final may be passed in (S_final may
-    be S0: in-place state update).  Runs on the current stream, asynchronously."""
+    be S0: in-place state update).  Runs on the current stream, asynchronously.
+    eta [B,H,T] fp32, if given, is a separate write strength (the C entry
+    gdn_chunk_fwd_eta); None means eta = beta."""
     torch = _torch()
     lib = load()
     B, H, T, dk = q.shape
@@ -91,6 +94,7 @@ def gdn_chunk_fwd(q, k, v, alpha, beta, S0=None, chunk_size: int = 64, o_dtype=N
     _check_tensor("v", v, (B, H, T, dv), q.dtype, dev)
     _check_tensor("alpha", alpha, (B, H, T), torch.float32, dev)
     _check_tensor("beta", beta, (B, H, T), torch.float32, dev)
+    _check_tensor("eta", eta, (B, H, T), torch.float32, dev)
     _check_tensor("S0", S0, (B, H, dv, dk), torch.float32, dev)
     if O is None:
         O = torch.empty((B, H, T, dv), dtype=o_dtype, device=dev)
@@ -101,18 +105,23 @@ def gdn_chunk_fwd(q, k, v, alpha, beta, S0=None, chunk_size: int = 64, o_dtype=N
     shape = make_shape(B, H, T, dk, dv, chunk_size, q.dtype, o_dtype)
     ws_bytes = gdn_chunk_fwd_workspace_bytes(shape)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None
-    st = lib.gdn_chunk_fwd(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha),
-                           _ptr(beta), _ptr(S0), _ptr(O), _ptr(S_final), _ptr(ws), ws_bytes,
-                           _stream_handle(dev, stream))
+    if eta is None:
+        st = lib.gdn_chunk_fwd(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha),
+                               _ptr(beta), _ptr(S0), _ptr(O), _ptr(S_final), _ptr(ws), ws_bytes,
+                               _stream_handle(dev, stream))
+    else:
+        st = lib.gdn_chunk_fwd_eta(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha),
+                                   _ptr(beta), _ptr(eta), _ptr(S0), _ptr(O), _ptr(S_final),
+                                   _ptr(ws), ws_bytes, _stream_handle(dev, stream))
     check(st)
     return O, S_final
 
 
 def gdn_recurrent_fwd(q, k, v, alpha, beta, S0=None, o_dtype=None, O=None, S_final=None,
-                      stream=None):
+                      stream=None, eta=None):
     """Token-by-token forward pass on the GPU (short T, e.g. a decode step).
     Same tensors and conventions as gdn_chunk_fwd; S_final may be S0 (the
-    state is then updated in place)."""
+    state is then updated in place); eta as for gdn_chunk_fwd."""
     torch = _torch()
     lib = load()
     B, H, T, dk = q.shape
@@ -126,6 +135,7 @@ def gdn_recurrent_fwd(q, k, v, alpha, beta, S0=None, o_dtype=None, O=None, S_fin
     _check_tensor("v", v, (B, H, T, dv), q.dtype, dev)
     _check_tensor("alpha", alpha, (B, H, T), torch.float32, dev)
     _check_tensor("beta", beta, (B, H, T), torch.float32, dev)
+    _check_tensor("eta", eta, (B, H, T), torch.float32, dev)
     _check_tensor("S0", S0, (B, H, dv, dk), torch.float32, dev)
     if O is None:
         O = torch.empty((B, H, T, dv), dtype=o_dtype, device=dev)
@@ -134,11 +144,26 @@ def gdn_recurrent_fwd(q, k, v, alpha, beta, S0=None, o_dtype=None, O=None, S_fin
         S_final = torch.empty((B, H, dv, dk), dtype=torch.float32, device=dev)
     _check_tensor("S_final", S_final, (B, H, dv, dk), torch.float32, dev)
     shape = make_shape(B, H, T, dk, dv, 1, q.dtype, o_dtype)
-    st = lib.gdn_recurrent_fwd(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha),
-                               _ptr(beta), _ptr(S0), _ptr(O), _ptr(S_final),
-                               _stream_handle(dev, stream))
+    if eta is None:
+        st = lib.gdn_recurrent_fwd(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha),
+                                   _ptr(beta), _ptr(S0), _ptr(O), _ptr(S_final),
+                                   _stream_handle(dev, stream))
+    else:
+        st = lib.gdn_recurrent_fwd_eta(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha),
+                                       _ptr(beta), _ptr(eta), _ptr(S0), _ptr(O), _ptr(S_final),
+                                       _stream_handle(dev, stream))
     check(st)
     return O, S_final
+
+
+def gdn_chunk_fwd_eta(q, k, v, alpha, beta, eta, S0=None, **kw):
+    """gdn_chunk_fwd with a separate write strength eta [B,H,T] (None: eta = beta)."""
+    return gdn_chunk_fwd(q, k, v, alpha, beta, S0, eta=eta, **kw)
+
+
+def gdn_recurrent_fwd_eta(q, k, v, alpha, beta, eta, S0=None, **kw):
+    """gdn_recurrent_fwd with a separate write strength eta [B,H,T] (None: eta = beta)."""
+    return gdn_recurrent_fwd(q, k, v, alpha, beta, S0, eta=eta, **kw)
 
 
 def gdn_chunk_prep(k, v, alpha, beta, chunk_size: int = 64, want=("T", "W", "U"), stream=None):

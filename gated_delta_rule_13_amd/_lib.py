@@ -21,8 +21,9 @@ STATUS = {
 }
 
 # Every symbol include/gdn.h declares.
-EXPORTS = ("gdn_chunk_fwd_workspace_bytes", "gdn_chunk_fwd", "gdn_chunk_prep",
-           "gdn_recurrent_fwd", "gdn_status_string", "gdn_last_error", "gdn_version")
+EXPORTS = ("gdn_chunk_fwd_workspace_bytes", "gdn_chunk_fwd", "gdn_chunk_fwd_eta",
+           "gdn_chunk_prep", "gdn_recurrent_fwd", "gdn_recurrent_fwd_eta",
+           "gdn_status_string", "gdn_last_error", "gdn_version")
 
 
 class GdnShape(ctypes.Structure):
@@ -58,6 +59,10 @@ def load():
     lib.gdn_chunk_prep.restype = ctypes.c_int
     lib.gdn_recurrent_fwd.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.gdn_recurrent_fwd.restype = ctypes.c_int
+    lib.gdn_chunk_fwd_eta.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+    lib.gdn_chunk_fwd_eta.restype = ctypes.c_int
+    lib.gdn_recurrent_fwd_eta.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.gdn_recurrent_fwd_eta.restype = ctypes.c_int
     lib.gdn_status_string.argtypes = [ctypes.c_int]
     lib.gdn_status_string.restype = ctypes.c_char_p
     lib.gdn_last_error.argtypes = []

@@ -96,8 +96,12 @@ using Launcher = void (*)(const gdn::FwdParams&, long, hipStream_t);
 
 template <int C, int DK, int NS>
 void launch_pipe(const gdn::FwdParams& p, long nblocks, hipStream_t st) {
-    hipLaunchKernelGGL((gdn::gdn_fwd_pipe_kernel<C, DK, NS>), dim3((unsigned)nblocks),
-                       dim3((NS + gdn::kPrepWaves) * 64), 0, st, p);
+    if (p.eta)
+        hipLaunchKernelGGL((gdn::gdn_fwd_pipe_kernel<C, DK, NS, true>), dim3((unsigned)nblocks),
+                           dim3((NS + gdn::kPrepWaves) * 64), 0, st, p);
+    else
+        hipLaunchKernelGGL((gdn::gdn_fwd_pipe_kernel<C, DK, NS, false>), dim3((unsigned)nblocks),
+                           dim3((NS + gdn::kPrepWaves) * 64), 0, st, p);
 }
 
 // Pipelined kernel: bf16 inputs, C in {32, 64}, d_k in {64, 128}.  NS scan
@@ -206,6 +210,14 @@ size_t gdn_chunk_fwd_workspace_bytes(const gdn_shape* s) {
 gdn_status gdn_chunk_fwd(const gdn_shape* s, const void* q, const void* k, const void* v,
                          const float* alpha, const float* beta, const float* S0, void* O,
                          float* S_final, void* workspace, size_t workspace_bytes, void* stream) {
+    return gdn_chunk_fwd_eta(s, q, k, v, alpha, beta, nullptr, S0, O, S_final, workspace,
+                             workspace_bytes, stream);
+}
+
+gdn_status gdn_chunk_fwd_eta(const gdn_shape* s, const void* q, const void* k, const void* v,
+                             const float* alpha, const float* beta, const float* eta,
+                             const float* S0, void* O, float* S_final, void* workspace,
+                             size_t workspace_bytes, void* stream) {
     (void)workspace;
     (void)workspace_bytes;
     g_last_error.clear();
@@ -214,7 +226,8 @@ gdn_status gdn_chunk_fwd(const gdn_shape* s, const void* q, const void* k, const
     if (!q || !k || !v || !beta || !O || !S_final)
         return fail(GDN_ERR_NULL_ARG, "q, k, v, beta, O and S_final are required");
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(O) || !aligned16(S_final) ||
-        (S0 && !aligned16(S0)) || !aligned16(beta) || (alpha && !aligned16(alpha)))
+        (S0 && !aligned16(S0)) || !aligned16(beta) || (alpha && !aligned16(alpha)) ||
+        (eta && !aligned16(eta)))
         return fail(GDN_ERR_UNSUPPORTED, "tensor pointers must be 16-byte aligned");
     const bool piped = pipe_supported(*s);
     const int nw = piped ? choose_scan_waves(*s) : choose_waves(*s);
@@ -226,6 +239,7 @@ gdn_status gdn_chunk_fwd(const gdn_shape* s, const void* q, const void* k, const
     p.v = v;
     p.alpha = alpha;
     p.beta = beta;
+    p.eta = eta;
     p.S0 = S0;
     p.O = O;
     p.S_final = S_final;
@@ -280,6 +294,12 @@ gdn_status gdn_chunk_prep(const gdn_shape* s, const void* k, const void* v, cons
 gdn_status gdn_recurrent_fwd(const gdn_shape* s, const void* q, const void* k, const void* v,
                              const float* alpha, const float* beta, const float* S0, void* O,
                              float* S_final, void* stream) {
+    return gdn_recurrent_fwd_eta(s, q, k, v, alpha, beta, nullptr, S0, O, S_final, stream);
+}
+
+gdn_status gdn_recurrent_fwd_eta(const gdn_shape* s, const void* q, const void* k, const void* v,
+                                 const float* alpha, const float* beta, const float* eta,
+                                 const float* S0, void* O, float* S_final, void* stream) {
     g_last_error.clear();
     if (!s) return fail(GDN_ERR_NULL_ARG, "shape is NULL");
     if (s->B < 1 || s->H < 1 || s->T < 1 || s->d_k < 1 || s->d_v < 1)
@@ -296,7 +316,8 @@ gdn_status gdn_recurrent_fwd(const gdn_shape* s, const void* q, const void* k, c
     if (!q || !k || !v || !beta || !O || !S_final)
         return fail(GDN_ERR_NULL_ARG, "q, k, v, beta, O and S_final are required");
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(O) || !aligned16(S_final) ||
-        (S0 && !aligned16(S0)) || !aligned16(beta) || (alpha && !aligned16(alpha)))
+        (S0 && !aligned16(S0)) || !aligned16(beta) || (alpha && !aligned16(alpha)) ||
+        (eta && !aligned16(eta)))
         return fail(GDN_ERR_UNSUPPORTED, "tensor pointers must be 16-byte aligned");
     gdn::RecParams p{};
     p.q = q;
@@ -304,6 +325,7 @@ gdn_status gdn_recurrent_fwd(const gdn_shape* s, const void* q, const void* k, c
     p.v = v;
     p.alpha = alpha;
     p.beta = beta;
+    p.eta = eta;
     p.S0 = S0;
     p.O = O;
     p.S_final = S_final;

@@ -43,6 +43,7 @@ struct FwdParams {
     int n_tiles;          // value-column tiles per head
     int o_bf16;           // O stored as bf16 (else fp32)
     int xcd_groups;       // pipelined kernel: place a head's tiles on one XCD
+    const float* eta;     // write strength; may be null: eta = beta
 };
 
 // LDS layout of one workgroup.  Rows are padded by 16 bytes.
@@ -66,6 +67,7 @@ struct alignas(16) Lds {
     float eg[C];                    // exp(g_r)
     float dec[C];                   // exp(g_last - g_r)
     float beta[C];
+    float eta[C];                   // write strength (= beta unless given)
     float glast;                    // exp(g_last)
 };
 
@@ -81,7 +83,7 @@ struct Stage {
     static constexpr int NKV = (KVEC + NTHR - 1) / NTHR;
     static constexpr int NVV = (VVEC + NTHR - 1) / NTHR;
     uint4 k[NKV], q[NKV], v[NVV];
-    float a, b;
+    float a, b, e;
 };
 
 template <int C, int DK, int NW, bool BF>
@@ -92,6 +94,7 @@ struct ChunkCtx {
     const In* vb;      // this sequence's v [T, dv]
     const float* ab;   // alpha [T] or null
     const float* bb;   // beta [T]
+    const float* eb;   // eta [T] or null (eta = beta)
     int T, dv, col0;   // col0: first value column of this tile
 };
 
@@ -128,12 +131,14 @@ __device__ __forceinline__ void load_chunk(Stage<C, DK, NW, BF>& st,
                     cx.vb + (size_t)(t0 + r) * cx.dv + cx.col0 + (size_t)c * S::EPV);
         }
     }
-    // padding tokens: alpha = 1, beta = 0 (identity transition)
+    // padding tokens: alpha = 1, beta = eta = 0 (identity transition)
     st.a = 1.f;
     st.b = 0.f;
+    st.e = 0.f;
     if (tid < Lc) {
         st.a = cx.ab ? cx.ab[t0 + tid] : 1.f;
         st.b = cx.bb[t0 + tid];
+        st.e = cx.eb ? cx.eb[t0 + tid] : st.b;
     }
 }
 
@@ -177,6 +182,7 @@ __device__ __forceinline__ void store_chunk(const Stage<C, DK, NW, BF>& st,
             s.eg[tid] = exp2f(g);
             s.dec[tid] = exp2f(gl - g);
             s.beta[tid] = st.b;
+            s.eta[tid] = st.e;
         }
         if (tid == 0) s.glast = exp2f(gl);
     }
@@ -236,8 +242,8 @@ __device__ __forceinline__ void gram_phase(Lds<C, DK, NW, BF>& s, int wave, int 
 //   diagonal 16 x 16 blocks: one lane per column, sequential over rows;
 //   block row R:  T_{R,c} = T_RR (sum_{m<R} A_{R,m} T_{m,c})  for c < R,
 // which is the same recurrence grouped by blocks.  All on VALU, fp32.
-// Then T diag(beta) is written (bf16: as hi + lo).
-template <int C, int DK, int NW, bool BF>
+// Then T diag(beta) (FOLD_BETA) or T is written (bf16: as hi + lo).
+template <bool FOLD_BETA, int C, int DK, int NW, bool BF>
 __device__ __forceinline__ void solve_phase(Lds<C, DK, NW, BF>& s, int tid, int wave, int lane) {
     constexpr int NT = C / 16;
     constexpr int NTHR = NW * 64;
@@ -279,7 +285,7 @@ __device__ __forceinline__ void solve_phase(Lds<C, DK, NW, BF>& s, int tid, int 
     for (int idx = tid; idx < C * C; idx += NTHR) {
         const int r = idx / C, i = idx % C;
         if ((i >> 4) <= (r >> 4)) {
-            const float x = s.Tm[r][i] * s.beta[i];
+            const float x = FOLD_BETA ? s.Tm[r][i] * s.beta[i] : s.Tm[r][i];
             if constexpr (BF) {
                 __bf16 hi, lo;
                 split_bf16(x, hi, lo);
@@ -341,6 +347,7 @@ __global__ __launch_bounds__(NW * 64) void gdn_fwd_kernel(FwdParams p) {
     cx.vb = reinterpret_cast<const In*>(p.v) + (size_t)bh * T * dv;
     cx.ab = p.alpha ? p.alpha + (size_t)bh * T : nullptr;
     cx.bb = p.beta + (size_t)bh * T;
+    cx.eb = p.eta ? p.eta + (size_t)bh * T : nullptr;
     cx.T = T;
     cx.dv = dv;
     cx.col0 = col_tile;
@@ -370,7 +377,7 @@ __global__ __launch_bounds__(NW * 64) void gdn_fwd_kernel(FwdParams p) {
 
         gram_phase(s, wave, n, h, true);
         __syncthreads();
-        solve_phase(s, tid, wave, lane);
+        solve_phase<false>(s, tid, wave, lane);
         __syncthreads();
 
         // ---- X = K S^T, Z = Q S^T (this wave's 16 columns) ----
@@ -406,17 +413,17 @@ __global__ __launch_bounds__(NW * 64) void gdn_fwd_kernel(FwdParams p) {
                 }
         }
 
-        // ---- pseudo-value input Y = V - diag(exp g) X ----
+        // ---- pseudo-value input Y = diag(eta) V - diag(beta) diag(exp g) X ----
         f32x4 Y[NT];
 #pragma unroll
         for (int rt = 0; rt < NT; ++rt)
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int r = 16 * rt + 4 * h + j;
-                Y[rt][j] = (float)s.V[r][16 * wave + n] - s.eg[r] * X[rt][j];
+                Y[rt][j] = s.eta[r] * (float)s.V[r][16 * wave + n] - s.beta[r] * s.eg[r] * X[rt][j];
             }
 
-        // ---- V' = T diag(beta) Y ----
+        // ---- V' = T Y ----
         f32x4 Vp[NT];
 #pragma unroll
         for (int rt = 0; rt < NT; ++rt) Vp[rt] = zero4();
@@ -570,6 +577,7 @@ __global__ __launch_bounds__(NW * 64) void gdn_prep_kernel(FwdParams p) {
     cx.vb = reinterpret_cast<const In*>(p.v) + (size_t)bh * T * dv;
     cx.ab = p.alpha ? p.alpha + (size_t)bh * T : nullptr;
     cx.bb = p.beta + (size_t)bh * T;
+    cx.eb = p.eta ? p.eta + (size_t)bh * T : nullptr;
     cx.T = T;
     cx.dv = dv;
     cx.col0 = col_tile;
@@ -582,7 +590,7 @@ __global__ __launch_bounds__(NW * 64) void gdn_prep_kernel(FwdParams p) {
     __syncthreads();
     gram_phase(s, wave, n, h, false);
     __syncthreads();
-    solve_phase(s, tid, wave, lane);
+    solve_phase<true>(s, tid, wave, lane);
     __syncthreads();
 
     if (tile == 0 && p.T_out) {

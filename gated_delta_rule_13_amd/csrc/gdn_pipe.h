@@ -6,11 +6,12 @@
 // evaluation order, both exact in real arithmetic:
 //
 // 1. T = (I - A)^{-1} is never formed.  The pseudo-values solve the unit
-//    lower-triangular system (I - A) V' = diag(beta) Y with
-//    Y = V - diag(exp g) K S^T (so that V' = U - W S^T), by forward
+//    lower-triangular system (I - A) V' = Y with
+//    Y = diag(eta) V - diag(beta) diag(exp g) K S^T (so that V' = U - W S^T;
+//    eta, the write strength, equals beta unless given), by forward
 //    substitution over 16-row blocks ("RNN的复兴03", section 2.3.1, grouped
 //    by blocks):
-//        V'_b = T_bb (diag(beta_b) Y_b + sum_{c<b} A_bc V'_c),
+//        V'_b = T_bb (Y_b + sum_{c<b} A_bc V'_c),
 //    where T_bb = (I - A_bb)^{-1} are the 16 x 16 diagonal blocks, solved by
 //    substitution on VALU (one lane per row of T_bb).  The coupling terms
 //    A_bc V'_c are dense 16 x 16 x 16 contractions and run on MFMA.
@@ -69,6 +70,26 @@ __device__ __forceinline__ void static_for(F&& f) {
 
 constexpr int kPrepWaves = 4;
 
+typedef __attribute__((ext_vector_type(2))) float f32x2;
+
+// An integer whose value the compiler may not reason about (no instruction
+// is emitted): used to keep it from proving 16-byte alignment of an offset.
+__device__ __forceinline__ int lds_opaque(int v) {
+    asm volatile("" : "+v"(v));
+    return v;
+}
+
+// Four floats at base + o (o a multiple of 4) read as two 8-byte halves.
+// For the scan's per-token vectors, which the 16 lanes of a row group read
+// at one address (a broadcast), a pair of 8-byte reads (ds_read2_b64)
+// measured faster than one 16-byte read (about 5 % of the kernel).
+__device__ __forceinline__ f32x4 lds_bcast4(const float* base, int o) {
+    o = lds_opaque(o);
+    const f32x2 a = *reinterpret_cast<const f32x2*>(base + o);
+    const f32x2 b = *reinterpret_cast<const f32x2*>(base + o + 2);
+    return f32x4{a[0], a[1], b[0], b[1]};
+}
+
 // eight consecutive elements [32 s + 8 h, +8) of an 8-byte aligned row, as two 8-byte reads
 __device__ __forceinline__ bf16x8 ld_nat8_b64(const __bf16* row, int s, int h) {
     const bf16x4 a = *reinterpret_cast<const bf16x4*>(row + 32 * s + 8 * h);
@@ -76,7 +97,7 @@ __device__ __forceinline__ bf16x8 ld_nat8_b64(const __bf16* row, int s, int h) {
     return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
-template <int C, int DK>
+template <int C, int DK, bool ETA>
 struct alignas(16) PipeLds {
     static constexpr int NT = C / 16;
     static constexpr int KP = DK + 4;   // row stride of key / query tiles (bf16): 8-byte aligned rows
@@ -108,6 +129,9 @@ struct alignas(16) PipeLds {
     float dec[2][C];                    // exp(g_last - g)
     float beta[2][C];
     float glast[2];                     // exp(g_last)
+    // with a separate write strength only: eta and beta exp(g)
+    float eta[ETA ? 2 : 1][ETA ? C : 4];
+    float bge[ETA ? 2 : 1][ETA ? C : 4];
 };
 
 // Chunk-local tile jobs of the prep waves.  Kinds: 0 = diagonal block of A
@@ -171,10 +195,13 @@ struct PrepJobs {
     }
 };
 
-template <int C, int DK, int NS>
+// ETA: a separate write strength is given (p.eta); otherwise eta = beta and
+// the substitution's right-hand side keeps the factored form
+// diag(beta) (V - diag(exp g) K S^T).
+template <int C, int DK, int NS, bool ETA>
 __global__ __launch_bounds__((NS + kPrepWaves) * 64) void gdn_fwd_pipe_kernel(FwdParams p) {
     constexpr int NP = kPrepWaves;
-    using L = PipeLds<C, DK>;
+    using L = PipeLds<C, DK, ETA>;
     using J = PrepJobs<C / 16, NP>;
     constexpr int NT = C / 16;
     constexpr int NK = DK / 16;
@@ -216,6 +243,7 @@ __global__ __launch_bounds__((NS + kPrepWaves) * 64) void gdn_fwd_pipe_kernel(Fw
     const __bf16* vb = reinterpret_cast<const __bf16*>(p.v) + (size_t)bh * T * dv;
     const float* ab = p.alpha ? p.alpha + (size_t)bh * T : nullptr;
     const float* bb = p.beta + (size_t)bh * T;
+    const float* eb = p.eta ? p.eta + (size_t)bh * T : nullptr;
     // per-head buffers: rows past the end of the sequence read as zero
     const buf_t kbuf = buffer_over(kb, (uint32_t)T * DK * 2);
     const buf_t qbuf = buffer_over(qb, (uint32_t)T * DK * 2);
@@ -236,7 +264,7 @@ __global__ __launch_bounds__((NS + kPrepWaves) * 64) void gdn_fwd_pipe_kernel(Fw
         // assigned row-fastest (one row per lane) so that the transposed copy
         // is written in contiguous runs; queries use the row-major order.
         uint4 stK[2][NKV], stQ[2][NKV];
-        float stA[2] = {1.f, 1.f}, stB[2] = {0.f, 0.f};
+        float stA[2] = {1.f, 1.f}, stB[2] = {0.f, 0.f}, stE[2] = {0.f, 0.f};
         f32x4 gacc[MAXJ];
 
         auto prep_load = [&](auto PAR, int cc) __attribute__((always_inline)) {
@@ -258,6 +286,7 @@ __global__ __launch_bounds__((NS + kPrepWaves) * 64) void gdn_fwd_pipe_kernel(Fw
                 const int tt = t0 + min(lane, Lc - 1);
                 stA[par] = ab ? ab[tt] : 1.f;
                 stB[par] = bb[tt];
+                if constexpr (ETA) stE[par] = eb[tt];
             }
         };
         auto prep_store = [&](auto PAR, int cc) __attribute__((always_inline)) {
@@ -288,7 +317,7 @@ __global__ __launch_bounds__((NS + kPrepWaves) * 64) void gdn_fwd_pipe_kernel(Fw
                 }
             });
             if (pw == 0) {
-                // padding tokens: alpha = 1, beta = 0 (identity transitions)
+                // padding tokens: alpha = 1, beta = eta = 0 (identity transitions)
                 const float a = lane < Lc ? stA[par] : 1.f;
                 const float l2 = (lane < C) ? __builtin_amdgcn_logf(a) : 0.f;
                 const float g = wave_inclusive_scan(l2, lane);
@@ -303,6 +332,10 @@ __global__ __launch_bounds__((NS + kPrepWaves) * 64) void gdn_fwd_pipe_kernel(Fw
                     s.eg[buf][lane] = __builtin_amdgcn_exp2f(g);
                     s.dec[buf][lane] = __builtin_amdgcn_exp2f(gl - g);
                     s.beta[buf][lane] = lane < Lc ? stB[par] : 0.f;
+                    if constexpr (ETA) {
+                        s.eta[buf][lane] = lane < Lc ? stE[par] : 0.f;
+                        s.bge[buf][lane] = lane < Lc ? stB[par] * __builtin_amdgcn_exp2f(g) : 0.f;
+                    }
                     s.er[buf][lane] = __builtin_amdgcn_exp2f(g - ref);
                     s.fi[buf][lane] = __builtin_amdgcn_exp2f(ref - g);
                 }
@@ -543,11 +576,15 @@ __global__ __launch_bounds__((NS + kPrepWaves) * 64) void gdn_fwd_pipe_kernel(Fw
                     bh_[b][cb] = *reinterpret_cast<const bf16x4*>(&s.Bh[buf][L::bidx(b, cb)][n][4 * h]);
                     bl_[b][cb] = *reinterpret_cast<const bf16x4*>(&s.Bl[buf][L::bidx(b, cb)][n][4 * h]);
                 }
-            f32x4 be_[NT], eg_[NT];
+            // right-hand side factors: (eta, beta exp g) or (beta, exp g)
+            // (the lanes of one row group read the same 16 bytes)
+            const float* f1b = ETA ? &s.eta[buf][0] : &s.beta[buf][0];
+            const float* f2b = ETA ? &s.bge[buf][0] : &s.eg[buf][0];
+            f32x4 f1_[NT], f2_[NT];
 #pragma unroll
             for (int b = 0; b < NT; ++b) {
-                be_[b] = *reinterpret_cast<const f32x4*>(&s.beta[buf][16 * b + 4 * h]);
-                eg_[b] = *reinterpret_cast<const f32x4*>(&s.eg[buf][16 * b + 4 * h]);
+                f1_[b] = lds_bcast4(f1b, 16 * b + 4 * h);
+                f2_[b] = lds_bcast4(f2b, 16 * b + 4 * h);
             }
             f32x4 Vp[NT];
             bf16x4 vph[NT], vpl[NT];
@@ -556,7 +593,9 @@ __global__ __launch_bounds__((NS + kPrepWaves) * 64) void gdn_fwd_pipe_kernel(Fw
                 f32x4 y;
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    y[j] = be_[b][j] * (bf16_bits_to_float(vnext[b][j]) - eg_[b][j] * X[b][j]);
+                    const float vv = bf16_bits_to_float(vnext[b][j]);
+                    y[j] = ETA ? f1_[b][j] * vv - f2_[b][j] * X[b][j]
+                               : f1_[b][j] * (vv - f2_[b][j] * X[b][j]);
                 }
                 f32x4 a1 = zero4(), a2 = zero4(), a3 = zero4();
 #pragma unroll

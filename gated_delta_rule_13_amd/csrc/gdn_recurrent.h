@@ -2,13 +2,15 @@
 // on gfx950, for short sequences such as a decode step.
 //
 // Per token ("从零开始的 GDN 推导", recurrent form, transposed to the
-// d_v x d_k state; "RNN的复兴03", section 1, with write strength = beta):
+// d_v x d_k state):
 //     u   = S_{t-1} k_t
-//     S_t = alpha_t (S_{t-1} - beta_t u k_t^T) + beta_t v_t k_t^T
-//         = alpha_t S_{t-1} + beta_t (v_t - alpha_t u) k_t^T
+//     S_t = alpha_t (S_{t-1} - beta_t u k_t^T) + eta_t v_t k_t^T
+//         = alpha_t S_{t-1} + (eta_t v_t - alpha_t beta_t u) k_t^T
 //     o_t = S_t q_t
+// with the write strength eta_t = beta_t unless it is given separately
+// ("RNN的复兴03", section 1).
 // Each row i of S evolves on its own (it needs only v_t[i] besides the shared
-// k_t, q_t, alpha_t, beta_t), so a group of LPR lanes owns one row: lane m
+// k_t, q_t, alpha_t, beta_t, eta_t), so a group of LPR lanes owns one row: lane m
 // keeps columns 4 m + 4 LPR j + e (j < J, e < 4) of that row in registers for
 // all T tokens, and the two row dot products are reduced across the group.
 // The state is read once and written once (in place when S_final == S0);
@@ -24,6 +26,7 @@ struct RecParams {
     const void* v;
     const float* alpha;     // may be null (alpha = 1)
     const float* beta;
+    const float* eta;       // may be null (eta = beta)
     const float* S0;        // may be null (zero state)
     void* O;
     float* S_final;
@@ -107,6 +110,7 @@ __global__ __launch_bounds__(kRecThreads) void gdn_recurrent_kernel(RecParams p)
         }
         const float a = p.alpha ? p.alpha[tok] : 1.f;
         const float b = p.beta[tok];
+        const float et = p.eta ? p.eta[tok] : b;
 #pragma unroll
         for (int r = 0; r < R; ++r) {
             const int row = row0 + GPB * r;
@@ -123,7 +127,7 @@ __global__ __launch_bounds__(kRecThreads) void gdn_recurrent_kernel(RecParams p)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) u = fmaf(S[r][j][e], kk[j][e], u);
             u = group_sum<LPR>(u);
-            const float coef = b * (vv - a * u);
+            const float coef = et * vv - a * b * u;
             float ot = 0.f;
 #pragma unroll
             for (int j = 0; j < J; ++j) {

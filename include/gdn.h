@@ -100,6 +100,22 @@ gdn_status gdn_chunk_fwd(const gdn_shape* s,
                          void* stream);
 
 /*
+ * The same pass with a separate write strength eta ("RNN的复兴03", section 1:
+ * erase strength beta, write strength eta):
+ *     S_t = alpha_t S_{t-1} (I - beta_t k_t k_t^T) + eta_t v_t k_t^T.
+ * eta [B, H, T] float, any finite value; NULL means eta = beta, which is
+ * exactly gdn_chunk_fwd.  beta = 0, eta = 1 gives gated linear attention
+ * ("从电路复杂性理论的角度分析大模型的可并行性和表达能力", GLA).
+ * Everything else as gdn_chunk_fwd.
+ */
+gdn_status gdn_chunk_fwd_eta(const gdn_shape* s,
+                             const void* q, const void* k, const void* v,
+                             const float* alpha, const float* beta, const float* eta,
+                             const float* S0, void* O, float* S_final,
+                             void* workspace, size_t workspace_bytes,
+                             void* stream);
+
+/*
  * Chunk-local quantities of the same method, for inspection and testing of
  * the intermediate stages.  For every chunk c (NT = ceil(T / C) chunks, the
  * last one zero-padded to C tokens):
@@ -141,6 +157,14 @@ gdn_status gdn_recurrent_fwd(const gdn_shape* s,
                              const float* alpha, const float* beta, const float* S0,
                              void* O, float* S_final,
                              void* stream);
+
+/* gdn_recurrent_fwd with a separate write strength eta (NULL means
+ * eta = beta), as for gdn_chunk_fwd_eta. */
+gdn_status gdn_recurrent_fwd_eta(const gdn_shape* s,
+                                 const void* q, const void* k, const void* v,
+                                 const float* alpha, const float* beta, const float* eta,
+                                 const float* S0, void* O, float* S_final,
+                                 void* stream);
 
 /* Static text for a status code. */
 const char* gdn_status_string(gdn_status st);
