@@ -616,8 +616,9 @@ __global__ __launch_bounds__((NS + kPrepWaves) * 64) void gdn_fwd_pipe_kernel(Fw
                 split4(Vp[b], vph[b], vpl[b]);
             }
             __syncthreads();
-            // the next chunk's values, consumed by the next phase A
-            if (c + 1 < nchunks) load_v(c + 1);
+            // the next chunk's values, consumed by the next phase A (past the
+            // last chunk every offset is out of range and reads zero)
+            load_v(c + 1);
             // ---- phase B: O^T = diag(exp g) Z^T + V'^T P^T (lane: row 16 rt + n, 4 columns) ----
             f32x4 PVt[NT];
 #pragma unroll
@@ -643,16 +644,6 @@ __global__ __launch_bounds__((NS + kPrepWaves) * 64) void gdn_fwd_pipe_kernel(Fw
                 for (int rt = 0; rt < NT; ++rt)
                     if (32 * ss <= 16 * rt + 15) PVt[rt] = mfma_bf16(vhi, pl[rt], PVt[rt]);
             }
-#pragma unroll
-            for (int rt = 0; rt < NT; ++rt) {
-                // rows past the end of the sequence fall outside the buffer (dropped)
-                const int r = 16 * rt + n;
-                const float e = s.eg[buf][r];
-                const f32x4 o = e * Zt[rt] + PVt[rt];
-                const uint32_t off = (uint32_t)((t0 + r) * dv + col0 + 4 * h) * osz;
-                if (p.o_bf16) buf_store(obuf, off, __builtin_convertvector(o, bf16x4));
-                else buf_store(obuf, off, o);
-            }
             // ---- S^T <- exp(g_last) S^T + K^T diag(exp(g_last - g)) V' ----
             const float gl = s.glast[buf];
 #pragma unroll
@@ -673,6 +664,23 @@ __global__ __launch_bounds__((NS + kPrepWaves) * 64) void gdn_fwd_pipe_kernel(Fw
                 for (int t = 0; t < NK; ++t) Sacc[t] = mfma_bf16(kt[t], vhi, Sacc[t]);
 #pragma unroll
                 for (int t = 0; t < NK; ++t) Sacc[t] = mfma_bf16(kt[t], vlo, Sacc[t]);
+            }
+            // output rows past the end of the sequence fall outside the buffer (dropped)
+            if (p.o_bf16) {
+#pragma unroll
+                for (int rt = 0; rt < NT; ++rt) {
+                    const int r = 16 * rt + n;
+                    const f32x4 o = s.eg[buf][r] * Zt[rt] + PVt[rt];
+                    buf_store(obuf, (uint32_t)((t0 + r) * dv + col0 + 4 * h) * 2,
+                              __builtin_convertvector(o, bf16x4));
+                }
+            } else {
+#pragma unroll
+                for (int rt = 0; rt < NT; ++rt) {
+                    const int r = 16 * rt + n;
+                    const f32x4 o = s.eg[buf][r] * Zt[rt] + PVt[rt];
+                    buf_store(obuf, (uint32_t)((t0 + r) * dv + col0 + 4 * h) * 4, o);
+                }
             }
             __syncthreads();
         }
