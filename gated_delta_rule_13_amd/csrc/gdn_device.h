@@ -50,11 +50,19 @@ __device__ __forceinline__ uint4 buf_load_16B(buf_t r, uint32_t off) {
     const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
     return make_uint4(v[0], v[1], v[2], v[3]);
 }
+// Streaming output stores (written once, never read back by the kernel).
+// Cache-policy bits of the gfx950 buffer store: 1 = sc0, 2 = nt, 16 = sc1.
+// 16-byte pieces go out non-temporal at system scope (written through, so
+// few dirty L2 lines are left for the end-of-kernel write-back); 8-byte
+// pieces only non-temporal (written through they would reach memory as
+// partial sectors).
+constexpr int kStoreNtSys = 1 | 2 | 16;
+constexpr int kStoreNt = 2;
 __device__ __forceinline__ void buf_store(buf_t r, uint32_t off, f32x4 v) {
-    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, (int)off, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, (int)off, 0, kStoreNtSys);
 }
 __device__ __forceinline__ void buf_store(buf_t r, uint32_t off, bf16x4 v) {
-    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, v), r, (int)off, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, v), r, (int)off, 0, kStoreNt);
 }
 
 // Round to bf16 (nearest-even) and the exact fp32 residual rounded again:
@@ -89,14 +97,28 @@ __device__ __forceinline__ bf16x8 ld_nat8(const __bf16* row, int s, int h) {
     return *reinterpret_cast<const bf16x8*>(row + 32 * s + 8 * h);
 }
 
-// Inclusive prefix sum over the first n lanes of a wave (n <= 64).
+// Value of lane (l - N) within the same row of 16 lanes, 0 where that lane
+// lies before the row (DPP row_shr:N).
+template <int N>
+__device__ __forceinline__ float row_shr_zero(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x110 + N,
+                                                                  0xf, 0xf, false));
+}
+__device__ __forceinline__ float lane_value(float x, int l) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), l));
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave: Hillis-Steele steps
+// 1, 2, 4, 8 within each row of 16 lanes (register-to-register, no LDS
+// round trip), then each row adds the totals of the rows before it.
 __device__ __forceinline__ float wave_inclusive_scan(float x, int lane) {
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        float y = __shfl_up(x, off, 64);
-        if (lane >= off) x += y;
-    }
-    return x;
+    x += row_shr_zero<1>(x);
+    x += row_shr_zero<2>(x);
+    x += row_shr_zero<4>(x);
+    x += row_shr_zero<8>(x);
+    const float t0 = lane_value(x, 15), t1 = lane_value(x, 31), t2 = lane_value(x, 47);
+    const int row = lane >> 4;
+    return x + ((row >= 1 ? t0 : 0.f) + (row >= 2 ? t1 : 0.f) + (row >= 3 ? t2 : 0.f));
 }
 
 }  // namespace gdn

@@ -19,12 +19,16 @@
 //    value columns and that slice of the fp32 state (S^T in MFMA
 //    accumulators); NP = 4 "prep" waves build the next chunk's chunk-local
 //    quantities (decay prefix, Gram matrix, masked scores, diagonal-block
-//    solves) while the scan waves consume the current chunk.  Per chunk c:
-//       phase A: scan  X = K S^T, Z^T = S Q^T, block substitution for V'
-//                prep  masked scores P of chunk c; stage chunk c + 1
-//       phase B: scan  O^T = Z^T + V'^T P^T, state update
-//                prep  Gram matrix of chunk c + 1 (MFMA), its A blocks and
-//                      diagonal-block solves T_bb
+//    solves) while the scan waves consume the current chunk.  Prep wave 0
+//    owns the per-token gates and the diagonal blocks, with the keys it
+//    needs for them in registers; prep waves 1..3 stage keys and queries in
+//    LDS and own the off-diagonal and score tiles.  Per chunk c:
+//       phase A: scan    X = K S^T, Z^T = S Q^T, block substitution for V'
+//                prep 0  decay vectors and diagonal blocks A_bb of chunk c + 1
+//                prep 1+ masked scores P of chunk c; stage chunk c + 1
+//       phase B: scan    O^T = Z^T + V'^T P^T, state update
+//                prep 0  diagonal-block solves T_bb of chunk c + 1
+//                prep 1+ Gram tiles of chunk c + 1 (MFMA), off-diagonal A blocks
 //    Keys, queries, transposed keys and the block matrices are double-buffered
 //    in LDS.  The output products are taken transposed (operands swapped) so
 //    that each lane ends with four consecutive columns of one output row.
@@ -134,11 +138,11 @@ struct alignas(16) PipeLds {
     float bge[ETA ? 2 : 1][ETA ? C : 4];
 };
 
-// Chunk-local tile jobs of the prep waves.  Kinds: 0 = diagonal block of A
-// (kept fp32 for the diagonal solve), 1 = off-diagonal block of A, 2 = block
-// of the masked scores P.  Prep wave 0 takes every diagonal block (it also
-// solves them); the other blocks go round-robin over waves 1..NP-1.
-// Encoding: (kind << 16) | (rt << 8) | ct for tile (rt, ct), ct <= rt.
+// Chunk-local tile jobs of prep waves 1..NP-1, round-robin.  Kinds:
+// 1 = off-diagonal block of A, 2 = block of the masked scores P (kind 0,
+// the diagonal blocks of A, belongs to prep wave 0, which computes them from
+// registers and solves them).  Encoding: (kind << 16) | (rt << 8) | ct for
+// tile (rt, ct), ct <= rt.
 template <int NT, int NP>
 struct PrepJobs {
     static constexpr int NPAIR = NT * (NT + 1) / 2;
@@ -174,13 +178,12 @@ struct PrepJobs {
     }
     static constexpr int owner(int k) { return 1 + k % (NP - 1); }
     static constexpr int count(int w) {
-        if (w == 0) return NT;
+        if (w == 0) return 0;
         int n = 0;
         for (int k = 0; k < NREST; ++k) n += owner(k) == w;
         return n;
     }
     static constexpr int job(int w, int j) {
-        if (w == 0) return (j << 8) | j;
         for (int k = 0; k < NREST; ++k)
             if (owner(k) == w) {
                 if (j == 0) return rest(k);
@@ -189,7 +192,7 @@ struct PrepJobs {
         return -1;
     }
     static constexpr int maxjobs() {
-        int m = 0;
+        int m = 1;
         for (int w = 0; w < NP; ++w) m = count(w) > m ? count(w) : m;
         return m;
     }
@@ -208,9 +211,10 @@ __global__ __launch_bounds__((NS + kPrepWaves) * 64) void gdn_fwd_pipe_kernel(Fw
     constexpr int DVT = 16 * NS;
     constexpr int NTHR = (NS + NP) * 64;
     constexpr int KV = C * DK / 8;        // 16-byte vectors in a key tile
-    constexpr int NKV = KV / (64 * NP);   // per prep lane
+    constexpr int NSTG = NP - 1;          // prep waves 1..NP-1 stage keys and queries
+    constexpr int NKV = (KV + 64 * NSTG - 1) / (64 * NSTG);   // per staging lane
+    constexpr int NDS = DK / 32;          // k-steps of a Gram tile
     constexpr int MAXJ = J::maxjobs();
-    static_assert(KV % (64 * NP) == 0, "key tile must split over the prep waves");
     static_assert(sizeof(L) <= 160 * 1024, "LDS budget");
     __shared__ L s;
 
@@ -222,7 +226,7 @@ __global__ __launch_bounds__((NS + kPrepWaves) * 64) void gdn_fwd_pipe_kernel(Fw
     const int h = lane >> 4;
     const bool scan = wave < NS;
     const int pw = wave - NS;             // prep wave 0..NP-1
-    const int plane = tid - NS * 64;      // 0..64*NP-1 on prep waves
+    const int plane = tid - (NS + 1) * 64;  // 0..64*NSTG-1 on prep waves 1..NP-1
 
     // Workgroups are dispatched round-robin over the 8 XCDs (L2 domains);
     // when the head count allows it, all value tiles of one head get block
@@ -259,74 +263,94 @@ __global__ __launch_bounds__((NS + kPrepWaves) * 64) void gdn_fwd_pipe_kernel(Fw
     // chunk (plus two in the prologue), so the barriers pair up by count.
     if (!scan) {
         // ============================ prep waves ============================
-        // Staging registers, two sets by chunk parity: chunk cc is loaded into
-        // set cc & 1 two iterations before it is written to LDS.  Keys are
-        // assigned row-fastest (one row per lane) so that the transposed copy
-        // is written in contiguous runs; queries use the row-major order.
+        // Prep waves 1..NP-1 stage keys and queries: registers, two sets by
+        // chunk parity (chunk cc is loaded into set cc & 1 two iterations
+        // before it is written to LDS).  Keys are assigned row-fastest (one
+        // row per lane) so that the transposed copy is written in contiguous
+        // runs; queries use the row-major order.  Prep wave 0 stages the
+        // per-token gates (same two sets) and keeps the next chunk's keys in
+        // registers in MFMA operand order for its diagonal Gram tiles.
         uint4 stK[2][NKV], stQ[2][NKV];
         float stA[2] = {1.f, 1.f}, stB[2] = {0.f, 0.f}, stE[2] = {0.f, 0.f};
         f32x4 gacc[MAXJ];
+        uint4 dK[NT][NDS];   // prep wave 0: keys of rows 16 rt + n, columns 32 ss + 8 h .. + 7
 
         auto prep_load = [&](auto PAR, int cc) __attribute__((always_inline)) {
             constexpr int par = decltype(PAR)::value;
             const int t0 = cc * C, Lc = min(C, T - t0);
-            static_for<0, NKV>([&](auto I) {
-                constexpr int i = decltype(I)::value;
-                const int vi = plane + i * 64 * NP;
-                {
-                    const int r = vi % C, c8 = (vi / C) * 8;
-                    stK[par][i] = buf_load_16B(kbuf, 2u * ((t0 + r) * DK + c8));
-                }
-                {
-                    const int r = vi / (DK / 8), c8 = (vi % (DK / 8)) * 8;
-                    stQ[par][i] = buf_load_16B(qbuf, 2u * ((t0 + r) * DK + c8));
-                }
-            });
             if (pw == 0) {
                 const int tt = t0 + min(lane, Lc - 1);
                 stA[par] = ab ? ab[tt] : 1.f;
                 stB[par] = bb[tt];
                 if constexpr (ETA) stE[par] = eb[tt];
+                return;
             }
+            static_for<0, NKV>([&](auto I) {
+                constexpr int i = decltype(I)::value;
+                const int vi = plane + i * 64 * NSTG;
+                if (i + 1 < NKV || vi < KV) {
+                    {
+                        const int r = vi % C, c8 = (vi / C) * 8;
+                        stK[par][i] = buf_load_16B(kbuf, 2u * ((t0 + r) * DK + c8));
+                    }
+                    {
+                        const int r = vi / (DK / 8), c8 = (vi % (DK / 8)) * 8;
+                        stQ[par][i] = buf_load_16B(qbuf, 2u * ((t0 + r) * DK + c8));
+                    }
+                }
+            });
+        };
+        // keys of chunk cc for prep wave 0's diagonal Gram tiles (rows past
+        // the end of the sequence read as zero)
+        auto diag_load = [&](int cc) __attribute__((always_inline)) {
+            const int t0 = cc * C;
+#pragma unroll
+            for (int rt = 0; rt < NT; ++rt)
+#pragma unroll
+                for (int ss = 0; ss < NDS; ++ss)
+                    dK[rt][ss] = buf_load_16B(kbuf, 2u * ((t0 + 16 * rt + n) * DK + 32 * ss + 8 * h));
         };
         auto prep_store = [&](auto PAR, int cc) __attribute__((always_inline)) {
             constexpr int par = decltype(PAR)::value;
             const int buf = cc & 1;
             const int Lc = min(C, T - cc * C);
-            static_for<0, NKV>([&](auto I) {
-                constexpr int i = decltype(I)::value;
-                const int vi = plane + i * 64 * NP;
-                {
-                    // rows past the end of the sequence were loaded as zeros
-                    const int r = vi % C, c8 = (vi / C) * 8;
-                    const uint4 kv = stK[par][i];
-                    *reinterpret_cast<uint2*>(&s.K[buf][r][c8]) = make_uint2(kv.x, kv.y);
-                    *reinterpret_cast<uint2*>(&s.K[buf][r][c8 + 4]) = make_uint2(kv.z, kv.w);
-                    static_for<0, 8>([&](auto X) {
-                        constexpr int x = decltype(X)::value;
-                        const unsigned word = x < 2 ? kv.x : x < 4 ? kv.y : x < 6 ? kv.z : kv.w;
-                        *reinterpret_cast<unsigned short*>(&s.Kt[buf][c8 + x][r]) =
-                            (unsigned short)(word >> (16 * (x & 1)));
-                    });
-                }
-                {
-                    const int r = vi / (DK / 8), c8 = (vi % (DK / 8)) * 8;
-                    const uint4 qv = stQ[par][i];
-                    *reinterpret_cast<uint2*>(&s.Q[buf][r][c8]) = make_uint2(qv.x, qv.y);
-                    *reinterpret_cast<uint2*>(&s.Q[buf][r][c8 + 4]) = make_uint2(qv.z, qv.w);
-                }
-            });
-            if (pw == 0) {
+            if (pw != 0) {
+                static_for<0, NKV>([&](auto I) {
+                    constexpr int i = decltype(I)::value;
+                    const int vi = plane + i * 64 * NSTG;
+                    if (i + 1 < NKV || vi < KV) {
+                        {
+                            // rows past the end of the sequence were loaded as zeros
+                            const int r = vi % C, c8 = (vi / C) * 8;
+                            const uint4 kv = stK[par][i];
+                            *reinterpret_cast<uint2*>(&s.K[buf][r][c8]) = make_uint2(kv.x, kv.y);
+                            *reinterpret_cast<uint2*>(&s.K[buf][r][c8 + 4]) = make_uint2(kv.z, kv.w);
+                            static_for<0, 8>([&](auto X) {
+                                constexpr int x = decltype(X)::value;
+                                const unsigned word = x < 2 ? kv.x : x < 4 ? kv.y : x < 6 ? kv.z : kv.w;
+                                *reinterpret_cast<unsigned short*>(&s.Kt[buf][c8 + x][r]) =
+                                    (unsigned short)(word >> (16 * (x & 1)));
+                            });
+                        }
+                        {
+                            const int r = vi / (DK / 8), c8 = (vi % (DK / 8)) * 8;
+                            const uint4 qv = stQ[par][i];
+                            *reinterpret_cast<uint2*>(&s.Q[buf][r][c8]) = make_uint2(qv.x, qv.y);
+                            *reinterpret_cast<uint2*>(&s.Q[buf][r][c8 + 4]) = make_uint2(qv.z, qv.w);
+                        }
+                    }
+                });
+            } else {
                 // padding tokens: alpha = 1, beta = eta = 0 (identity transitions)
                 const float a = lane < Lc ? stA[par] : 1.f;
                 const float l2 = (lane < C) ? __builtin_amdgcn_logf(a) : 0.f;
                 const float g = wave_inclusive_scan(l2, lane);
-                const float gl = __shfl(g, C - 1, 64);
+                const float gl = lane_value(g, C - 1);
                 // exp(g_r - g_i) = 2^(g2_r - ref) * 2^(ref - g2_i) with ref the middle
                 // of the chunk; used when the chunk's decay range keeps both factors
                 // far inside fp32 (else the formation exponentiates each ratio).
-                const float ref = __shfl(g, C / 2, 64);
-                const float g0 = __shfl(g, 0, 64);
+                const float ref = lane_value(g, C / 2);
+                const float g0 = lane_value(g, 0);
                 if (lane < C) {
                     s.g2[buf][lane] = g;
                     s.eg[buf][lane] = __builtin_amdgcn_exp2f(g);
@@ -414,6 +438,43 @@ __global__ __launch_bounds__((NS + kPrepWaves) * 64) void gdn_fwd_pipe_kernel(Fw
                 }
             });
         };
+        // Prep wave 0: the diagonal blocks A_bb of chunk cc, Gram tiles from the
+        // keys held in registers (the same register is both MFMA operands),
+        // formed in fp32 for the solve.  Lane holds row r = 16 rt + n,
+        // columns 16 rt + 4 h + e.
+        auto diag_blocks = [&](int cc) __attribute__((always_inline)) {
+            const int buf = cc & 1;
+            auto run = [&](auto SEP) __attribute__((always_inline)) {
+                constexpr bool sep = decltype(SEP)::value;
+                static_for<0, NT>([&](auto RT) {
+                    constexpr int rt = decltype(RT)::value;
+                    f32x4 acc = zero4();
+#pragma unroll
+                    for (int ss = 0; ss < NDS; ++ss) {
+                        const bf16x8 kv = __builtin_bit_cast(bf16x8, dK[rt][ss]);
+                        acc = mfma_bf16(kv, kv, acc);
+                    }
+                    const int r = 16 * rt + n;
+                    const int i0 = 16 * rt + 4 * h;
+                    const float br = s.beta[buf][r];
+                    f32x4 d;
+                    if constexpr (sep) {
+                        d = s.er[buf][r] * *reinterpret_cast<const f32x4*>(&s.fi[buf][i0]);
+                    } else {
+                        const float g2r = s.g2[buf][r];
+                        const f32x4 g2i = *reinterpret_cast<const f32x4*>(&s.g2[buf][i0]);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) d[e] = __builtin_amdgcn_exp2f(g2r - g2i[e]);
+                    }
+                    f32x4 v;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) v[e] = (i0 + e < r) ? -br * d[e] * acc[e] : 0.f;
+                    *reinterpret_cast<f32x4*>(&s.Ad[rt][n][4 * h]) = v;
+                });
+            };
+            if (s.sep[buf]) run(std::true_type{});
+            else run(std::false_type{});
+        };
         // T_bb = (I - A_bb)^{-1}, all diagonal blocks at once: lane (b, i)
         // computes row i of T_bb from T = I + T A, i.e. the transposed
         // unit triangular system, by substitution from the last column down:
@@ -468,43 +529,67 @@ __global__ __launch_bounds__((NS + kPrepWaves) * 64) void gdn_fwd_pipe_kernel(Fw
         // job index is a compile-time constant within one loop.
         auto prep_role = [&](auto W) __attribute__((always_inline)) {
             constexpr int w = decltype(W)::value;
-            // Gram tiles of chunk cc, then its A blocks and diagonal solves
-            // (written to the block buffer of cc's parity).  The score tiles
-            // stay in registers until the next phase A.
+            // waves 1..NP-1: Gram tiles of chunk cc and its off-diagonal A
+            // blocks; the score tiles stay in registers until the next phase A
             auto chunk_matrices = [&](int cc) __attribute__((always_inline)) {
                 gram(W, cc);
                 if (s.sep[cc & 1]) form(W, std::true_type{}, std::false_type{}, cc);
                 else form(W, std::false_type{}, std::false_type{}, cc);
-                if constexpr (w == 0) {
-                    wave_lds_sync();
-                    diag_solve(cc);
-                }
+            };
+            // wave 0: decay vectors of chunk cc and its diagonal blocks A_bb;
+            // then the keys of chunk cc + 1 into registers
+            auto diag_work = [&](auto PAR, int cc) __attribute__((always_inline)) {
+                prep_store(PAR, cc);
+                wave_lds_sync();
+                diag_blocks(cc);
+                if (cc + 1 < nchunks) diag_load(cc + 1);
             };
             // one pipeline step; PAR = parity of chunk c
             auto step = [&](auto PAR, int c) __attribute__((always_inline)) {
                 constexpr int nxt = decltype(PAR)::value ^ 1;
-                // ---- phase A: scores of chunk c; stage chunk c + 1 ----
-                if (s.sep[c & 1]) form(W, std::true_type{}, std::true_type{}, c);
-                else form(W, std::false_type{}, std::true_type{}, c);
-                if (c + 1 < nchunks) {
-                    prep_store(std::integral_constant<int, nxt>{}, c + 1);
-                    if (c + 3 < nchunks) prep_load(std::integral_constant<int, nxt>{}, c + 3);
+                // ---- phase A: scores of chunk c; stage chunk c + 1; its
+                //      decay vectors and diagonal blocks ----
+                if constexpr (w == 0) {
+                    if (c + 1 < nchunks) {
+                        diag_work(std::integral_constant<int, nxt>{}, c + 1);
+                        if (c + 3 < nchunks) prep_load(std::integral_constant<int, nxt>{}, c + 3);
+                    }
+                } else {
+                    if (s.sep[c & 1]) form(W, std::true_type{}, std::true_type{}, c);
+                    else form(W, std::false_type{}, std::true_type{}, c);
+                    if (c + 1 < nchunks) {
+                        prep_store(std::integral_constant<int, nxt>{}, c + 1);
+                        if (c + 3 < nchunks) prep_load(std::integral_constant<int, nxt>{}, c + 3);
+                    }
                 }
                 __syncthreads();
-                // ---- phase B: Gram matrix, A blocks and T_bb of chunk c + 1 ----
-                if (c + 1 < nchunks) chunk_matrices(c + 1);
+                // ---- phase B: chunk c + 1's Gram tiles and off-diagonal A
+                //      blocks (waves 1..), T_bb of its diagonal blocks (wave 0) ----
+                if (c + 1 < nchunks) {
+                    if constexpr (w != 0) chunk_matrices(c + 1);
+                    else diag_solve(c + 1);
+                }
                 __syncthreads();
             };
-            prep_load(std::integral_constant<int, 0>{}, 0);
-            if (nchunks > 1) prep_load(std::integral_constant<int, 1>{}, 1);
-            prep_store(std::integral_constant<int, 0>{}, 0);
-            if (nchunks > 2) prep_load(std::integral_constant<int, 0>{}, 2);
+            constexpr auto P0 = std::integral_constant<int, 0>{};
+            constexpr auto P1 = std::integral_constant<int, 1>{};
+            prep_load(P0, 0);
+            if (nchunks > 1) prep_load(P1, 1);
+            if constexpr (w == 0) {
+                diag_load(0);
+                diag_work(P0, 0);
+                wave_lds_sync();
+                diag_solve(0);
+            } else {
+                prep_store(P0, 0);
+            }
+            if (nchunks > 2) prep_load(P0, 2);
             __syncthreads();
-            chunk_matrices(0);
+            if constexpr (w != 0) chunk_matrices(0);
             __syncthreads();
             for (int c = 0; c < nchunks; c += 2) {
-                step(std::integral_constant<int, 0>{}, c);
-                if (c + 1 < nchunks) step(std::integral_constant<int, 1>{}, c + 1);
+                step(P0, c);
+                if (c + 1 < nchunks) step(P1, c + 1);
             }
         };
         switch (pw) {
