@@ -14,7 +14,8 @@
 //        V'_b = T_bb (Y_b + sum_{c<b} A_bc V'_c),
 //    where T_bb = (I - A_bb)^{-1} are the 16 x 16 diagonal blocks, solved by
 //    substitution on VALU (one lane per row of T_bb).  The coupling terms
-//    A_bc V'_c are dense 16 x 16 x 16 contractions and run on MFMA.
+//    A_bc V'_c are dense 16 x 16 x 16 contractions; each one's bf16 hi / lo
+//    products run as two 16 x 16 x 32 MFMAs (operands concatenated along k).
 // 2. Work is split by role inside the workgroup: NS "scan" waves each own 16
 //    value columns and that slice of the fp32 state (S^T in MFMA
 //    accumulators); NP = 4 "prep" waves build the next chunk's chunk-local
@@ -43,11 +44,8 @@
 
 namespace gdn {
 
-typedef __attribute__((ext_vector_type(4))) short s16x4;
-
-__device__ __forceinline__ f32x4 mfma16_bf16(bf16x4 a, bf16x4 b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a),
-                                                     __builtin_bit_cast(s16x4, b), c, 0, 0, 0);
+__device__ __forceinline__ bf16x8 cat8(bf16x4 a, bf16x4 b) {
+    return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
 __device__ __forceinline__ void split4(f32x4 x, bf16x4& hi, bf16x4& lo) {
@@ -682,22 +680,22 @@ __global__ __launch_bounds__((NS + kPrepWaves) * 64) void gdn_fwd_pipe_kernel(Fw
                     y[j] = ETA ? f1_[b][j] * vv - f2_[b][j] * X[b][j]
                                : f1_[b][j] * (vv - f2_[b][j] * X[b][j]);
                 }
-                f32x4 a1 = zero4(), a2 = zero4(), a3 = zero4();
+                // The three hi / lo products of a block pair as two k = 32
+                // MFMAs: (Bh, Bl) . (vh, vh) with both operands concatenated
+                // along k the same way, and (Bh, 0) . (vl, 0).  Every product
+                // on one accumulator is the same k = 32 instruction: chaining a
+                // 16 x 16 x 16 MFMA onto a 16 x 16 x 32 result gave wrong sums.
+                const bf16x4 z4 = {};
+                f32x4 rhs = y;
 #pragma unroll
                 for (int cb = 0; cb < b; ++cb) {
-                    a1 = mfma16_bf16(bh_[b][cb], vph[cb], a1);
-                    a2 = mfma16_bf16(bh_[b][cb], vpl[cb], a2);
-                    a3 = mfma16_bf16(bl_[b][cb], vph[cb], a3);
+                    rhs = mfma_bf16(cat8(bh_[b][cb], bl_[b][cb]), cat8(vph[cb], vph[cb]), rhs);
+                    rhs = mfma_bf16(cat8(bh_[b][cb], z4), cat8(vpl[cb], z4), rhs);
                 }
-                const f32x4 rhs = y + a1 + a2 + a3;
                 bf16x4 rh, rl;
                 split4(rhs, rh, rl);
-                const bf16x4 th = bh_[b][b];
-                const bf16x4 tl = bl_[b][b];
-                const f32x4 t1 = mfma16_bf16(th, rh, zero4());
-                const f32x4 t2 = mfma16_bf16(th, rl, zero4());
-                const f32x4 t3 = mfma16_bf16(tl, rh, zero4());
-                Vp[b] = t1 + t2 + t3;
+                Vp[b] = mfma_bf16(cat8(bh_[b][b], bl_[b][b]), cat8(rh, rh), zero4());
+                Vp[b] = mfma_bf16(cat8(bh_[b][b], z4), cat8(rl, z4), Vp[b]);
                 split4(Vp[b], vph[b], vpl[b]);
             }
             __syncthreads();
