@@ -28,7 +28,9 @@
 //                prep 0  decay vectors and diagonal blocks A_bb of chunk c + 1
 //                prep 1+ masked scores P of chunk c; stage chunk c + 1
 //       phase B: scan    O^T = Z^T + V'^T P^T, state update
-//                prep 0  diagonal-block solves T_bb of chunk c + 1
+//                prep 0  diagonal-block solves T_bb of chunk c + 1; with one
+//                        or two scan waves also chunk c + 1's values, written
+//                        transposed into LDS for the scan's next phase A
 //                prep 1+ Gram tiles of chunk c + 1 (MFMA), off-diagonal A blocks
 //    Keys, queries, transposed keys and the block matrices are double-buffered
 //    in LDS.  The output products are taken transposed (operands swapped) so
@@ -99,7 +101,12 @@ __device__ __forceinline__ bf16x8 ld_nat8_b64(const __bf16* row, int s, int h) {
     return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
-template <int C, int DK, bool ETA>
+// Whether prep wave 0 stages the value tile in LDS (VT) for the scan waves;
+// with four scan waves the tile is twice as large and the scan waves load
+// their values themselves.
+constexpr bool pipe_stages_values(int ns) { return ns <= 2; }
+
+template <int C, int DK, int NS, bool ETA>
 struct alignas(16) PipeLds {
     static constexpr int NT = C / 16;
     static constexpr int KP = DK + 4;   // row stride of key / query tiles (bf16): 8-byte aligned rows
@@ -134,6 +141,12 @@ struct alignas(16) PipeLds {
     // with a separate write strength only: eta and beta exp(g)
     float eta[ETA ? 2 : 1][ETA ? C : 4];
     float bge[ETA ? 2 : 1][ETA ? C : 4];
+    // the workgroup's 16 NS value columns of one chunk, transposed (a row per
+    // column, C + 4 row stride as for the scores): a scan lane reads its four
+    // consecutive tokens of one column as one 8-byte read.  Last, so that the
+    // offsets of the members above do not depend on it.
+    static constexpr bool VST = pipe_stages_values(NS);
+    __bf16 VT[VST ? 16 * NS : 1][VST ? CP : 8];
 };
 
 // Chunk-local tile jobs of prep waves 1..NP-1, round-robin.  Kinds:
@@ -202,7 +215,8 @@ struct PrepJobs {
 template <int C, int DK, int NS, bool ETA>
 __global__ __launch_bounds__((NS + kPrepWaves) * 64) void gdn_fwd_pipe_kernel(FwdParams p) {
     constexpr int NP = kPrepWaves;
-    using L = PipeLds<C, DK, ETA>;
+    using L = PipeLds<C, DK, NS, ETA>;
+    constexpr bool VST = L::VST;
     using J = PrepJobs<C / 16, NP>;
     constexpr int NT = C / 16;
     constexpr int NK = DK / 16;
@@ -269,6 +283,41 @@ __global__ __launch_bounds__((NS + kPrepWaves) * 64) void gdn_fwd_pipe_kernel(Fw
         // per-token gates (same two sets) and keeps the next chunk's keys in
         // registers in MFMA operand order for its diagonal Gram tiles.
         uint4 stK[2][NKV], stQ[2][NKV];
+        // prep wave 0 (VST): the next chunk's value tile (16 NS columns),
+        // loaded one chunk ahead and written transposed in phase B
+        constexpr int VV = C * 2 * NS;          // 16-byte vectors in a value tile
+        constexpr int NVV = VST ? (VV + 63) / 64 : 1;
+        uint4 stV[NVV];
+        const buf_t vbuf_p = buffer_over(vb, (uint32_t)T * dv * 2);
+        const int vcol0 = tile * DVT;
+        // rows past the end of the sequence read as zero
+        auto v_load = [&](int cc) __attribute__((always_inline)) {
+            const int t0 = cc * C;
+            static_for<0, NVV>([&](auto I) {
+                constexpr int i = decltype(I)::value;
+                const int vi = lane + i * 64;
+                if (i + 1 < NVV || vi < VV) {
+                    const int r = vi % C, c8 = (vi / C) * 8;
+                    stV[i] = buf_load_16B(vbuf_p, 2u * ((t0 + r) * dv + vcol0 + c8));
+                }
+            });
+        };
+        auto v_store = [&]() __attribute__((always_inline)) {
+            static_for<0, NVV>([&](auto I) {
+                constexpr int i = decltype(I)::value;
+                const int vi = lane + i * 64;
+                if (i + 1 < NVV || vi < VV) {
+                    const int r = vi % C, c8 = (vi / C) * 8;
+                    const uint4 vv = stV[i];
+                    static_for<0, 8>([&](auto X) {
+                        constexpr int x = decltype(X)::value;
+                        const unsigned word = x < 2 ? vv.x : x < 4 ? vv.y : x < 6 ? vv.z : vv.w;
+                        *reinterpret_cast<unsigned short*>(&s.VT[c8 + x][r]) =
+                            (unsigned short)(word >> (16 * (x & 1)));
+                    });
+                }
+            });
+        };
         float stA[2] = {1.f, 1.f}, stB[2] = {0.f, 0.f}, stE[2] = {0.f, 0.f};
         f32x4 gacc[MAXJ];
         uint4 dK[NT][NDS];   // prep wave 0: keys of rows 16 rt + n, columns 32 ss + 8 h .. + 7
@@ -564,18 +613,30 @@ __global__ __launch_bounds__((NS + kPrepWaves) * 64) void gdn_fwd_pipe_kernel(Fw
                 // ---- phase B: chunk c + 1's Gram tiles and off-diagonal A
                 //      blocks (waves 1..), T_bb of its diagonal blocks (wave 0) ----
                 if (c + 1 < nchunks) {
-                    if constexpr (w != 0) chunk_matrices(c + 1);
-                    else diag_solve(c + 1);
+                    if constexpr (w != 0) {
+                        chunk_matrices(c + 1);
+                    } else {
+                        if constexpr (VST) {
+                            v_store();
+                            if (c + 2 < nchunks) v_load(c + 2);
+                        }
+                        diag_solve(c + 1);
+                    }
                 }
                 __syncthreads();
             };
             constexpr auto P0 = std::integral_constant<int, 0>{};
             constexpr auto P1 = std::integral_constant<int, 1>{};
+            if constexpr (w == 0 && VST) v_load(0);
             prep_load(P0, 0);
             if (nchunks > 1) prep_load(P1, 1);
             if constexpr (w == 0) {
                 diag_load(0);
                 diag_work(P0, 0);
+                if constexpr (VST) {
+                    v_store();
+                    if (nchunks > 1) v_load(1);
+                }
                 wave_lds_sync();
                 diag_solve(0);
             } else {
@@ -599,18 +660,21 @@ __global__ __launch_bounds__((NS + kPrepWaves) * 64) void gdn_fwd_pipe_kernel(Fw
     } else {
         // ============================ scan waves ============================
         f32x4 Sacc[NK];           // Sacc[t][j] = S[col0 + n][16 t + 4 h + j]
-        uint32_t vnext[NT][4];    // this lane's values of the next chunk, bf16 bits (zero past the end)
+        // without VST: this lane's values of the next chunk, bf16 bits (zero past the end)
+        uint32_t vnext[VST ? 1 : NT][4];
         const buf_t vbuf = buffer_over(vb, (uint32_t)T * dv * 2);
         const uint32_t vlane = 2u * (4 * h * dv + col0 + n);
         auto load_v = [&](int cc) __attribute__((always_inline)) {
-            const int t0 = cc * C;
-            static_for<0, NT>([&](auto RT) {
-                constexpr int rt = decltype(RT)::value;
-                static_for<0, 4>([&](auto JJ) {
-                    constexpr int j = decltype(JJ)::value;
-                    vnext[rt][j] = buf_load_bf16_bits(vbuf, vlane + 2u * (t0 + 16 * rt + j) * dv);
+            if constexpr (!VST) {
+                const int t0 = cc * C;
+                static_for<0, NT>([&](auto RT) {
+                    constexpr int rt = decltype(RT)::value;
+                    static_for<0, 4>([&](auto JJ) {
+                        constexpr int j = decltype(JJ)::value;
+                        vnext[rt][j] = buf_load_bf16_bits(vbuf, vlane + 2u * (t0 + 16 * rt + j) * dv);
+                    });
                 });
-            });
+            }
         };
         const int osz = p.o_bf16 ? 2 : 4;
         const buf_t obuf = buffer_over(reinterpret_cast<const char*>(p.O) + (size_t)bh * T * dv * osz,
@@ -627,6 +691,14 @@ __global__ __launch_bounds__((NS + kPrepWaves) * 64) void gdn_fwd_pipe_kernel(Fw
             const int buf = c & 1;
             const int t0 = c * C;
             // ---- phase A: X = K S^T, Z^T = S Q^T ----
+            // with VST this chunk's values come from LDS: lane (n, h) reads
+            // tokens 16 b + 4 h + j of its column (zero past the end)
+            bf16x4 vcur[VST ? NT : 1];
+            if constexpr (VST) {
+#pragma unroll
+                for (int b = 0; b < NT; ++b)
+                    vcur[b] = *reinterpret_cast<const bf16x4*>(&s.VT[16 * wave + n][16 * b + 4 * h]);
+            }
             f32x4 X[NT], Zt[NT];
 #pragma unroll
             for (int rt = 0; rt < NT; ++rt) { X[rt] = zero4(); Zt[rt] = zero4(); }
@@ -676,7 +748,9 @@ __global__ __launch_bounds__((NS + kPrepWaves) * 64) void gdn_fwd_pipe_kernel(Fw
                 f32x4 y;
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    const float vv = bf16_bits_to_float(vnext[b][j]);
+                    float vv;
+                    if constexpr (VST) vv = (float)vcur[b][j];
+                    else vv = bf16_bits_to_float(vnext[b][j]);
                     y[j] = ETA ? f1_[b][j] * vv - f2_[b][j] * X[b][j]
                                : f1_[b][j] * (vv - f2_[b][j] * X[b][j]);
                 }
