@@ -94,29 +94,33 @@ __device__ __forceinline__ f32x4 lds_bcast4(const float* base, int o) {
     return f32x4{a[0], a[1], b[0], b[1]};
 }
 
-// eight consecutive elements [32 s + 8 h, +8) of an 8-byte aligned row, as two 8-byte reads
-__device__ __forceinline__ bf16x8 ld_nat8_b64(const __bf16* row, int s, int h) {
-    const bf16x4 a = *reinterpret_cast<const bf16x4*>(row + 32 * s + 8 * h);
-    const bf16x4 b = *reinterpret_cast<const bf16x4*>(row + 32 * s + 8 * h + 4);
-    return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
-}
-
 // Whether prep wave 0 stages the value tile in LDS (VT) for the scan waves;
 // with four scan waves the tile is twice as large and the scan waves load
 // their values themselves.
 constexpr bool pipe_stages_values(int ns) { return ns <= 2; }
 
+// Position in an LDS key / query row of natural element k (a multiple of 4):
+// within each 32-element block, group g = (k mod 32) / 4 of four elements
+// goes to 8 g for g < 4 and to 8 (g - 4) + 4 for g >= 4.
+__device__ __forceinline__ int kq_pos(int k) {
+    const int g = (k & 31) >> 2;
+    return (k & ~31) + (g < 4 ? 8 * g : 8 * (g - 4) + 4);
+}
+
 template <int C, int DK, int NS, bool ETA>
 struct alignas(16) PipeLds {
     static constexpr int NT = C / 16;
-    static constexpr int KP = DK + 4;   // row stride of key / query tiles (bf16): 8-byte aligned rows
+    // Key / query rows: each 32-element block stored in the scan's k-order
+    // (elements 4h..4h+3 then 16+4h..16+4h+3 for h = 0..3), so that any MFMA
+    // operand slice is one aligned 16-byte read; row stride d_k + 8 (an odd
+    // multiple of 16 bytes modulo 128: 16-byte reads of 8 rows hit distinct banks).
+    static constexpr int KP = DK + 8;
     // Row strides against LDS bank conflicts (32 banks of 4 bytes; an 8-byte
     // access serves 16 lanes per pass): 8-byte column slices of 16
     // consecutive rows hit distinct banks when the stride is an odd multiple
     // of 8 bytes modulo 128, as for C + 4 bf16 (C = 32, 64) and 20 bf16;
     // 16-byte slices of 8 rows when it is an odd multiple of 16, as for
-    // 20 floats.  Key / query rows (d_k + 4 bf16) are only 8-byte aligned,
-    // so they are written and read in 8-byte pieces.
+    // 20 floats and d_k + 8 bf16.
     static constexpr int CP = C + 4;    // row stride of C-wide rows (bf16)
     static constexpr int BP = 20;       // row stride of 16 x 16 blocks (bf16 and fp32)
     __bf16 K[2][C][KP];
@@ -370,8 +374,8 @@ __global__ __launch_bounds__((NS + kPrepWaves) * 64) void gdn_fwd_pipe_kernel(Fw
                             // rows past the end of the sequence were loaded as zeros
                             const int r = vi % C, c8 = (vi / C) * 8;
                             const uint4 kv = stK[par][i];
-                            *reinterpret_cast<uint2*>(&s.K[buf][r][c8]) = make_uint2(kv.x, kv.y);
-                            *reinterpret_cast<uint2*>(&s.K[buf][r][c8 + 4]) = make_uint2(kv.z, kv.w);
+                            *reinterpret_cast<uint2*>(&s.K[buf][r][kq_pos(c8)]) = make_uint2(kv.x, kv.y);
+                            *reinterpret_cast<uint2*>(&s.K[buf][r][kq_pos(c8 + 4)]) = make_uint2(kv.z, kv.w);
                             static_for<0, 8>([&](auto X) {
                                 constexpr int x = decltype(X)::value;
                                 const unsigned word = x < 2 ? kv.x : x < 4 ? kv.y : x < 6 ? kv.z : kv.w;
@@ -382,8 +386,8 @@ __global__ __launch_bounds__((NS + kPrepWaves) * 64) void gdn_fwd_pipe_kernel(Fw
                         {
                             const int r = vi / (DK / 8), c8 = (vi % (DK / 8)) * 8;
                             const uint4 qv = stQ[par][i];
-                            *reinterpret_cast<uint2*>(&s.Q[buf][r][c8]) = make_uint2(qv.x, qv.y);
-                            *reinterpret_cast<uint2*>(&s.Q[buf][r][c8 + 4]) = make_uint2(qv.z, qv.w);
+                            *reinterpret_cast<uint2*>(&s.Q[buf][r][kq_pos(c8)]) = make_uint2(qv.x, qv.y);
+                            *reinterpret_cast<uint2*>(&s.Q[buf][r][kq_pos(c8 + 4)]) = make_uint2(qv.z, qv.w);
                         }
                     }
                 });
@@ -430,7 +434,8 @@ __global__ __launch_bounds__((NS + kPrepWaves) * 64) void gdn_fwd_pipe_kernel(Fw
                 f32x4 acc = zero4();
 #pragma unroll
                 for (int ss = 0; ss < DK / 32; ++ss)
-                    acc = mfma_bf16(ld_nat8_b64(arow, ss, h), ld_nat8_b64(brow, ss, h), acc);
+                    acc = mfma_bf16(*reinterpret_cast<const bf16x8*>(arow + 32 * ss + 8 * h),
+                                    *reinterpret_cast<const bf16x8*>(brow + 32 * ss + 8 * h), acc);
                 gacc[j] = acc;
             });
         };
@@ -709,8 +714,8 @@ __global__ __launch_bounds__((NS + kPrepWaves) * 64) void gdn_fwd_pipe_kernel(Fw
                 bf16x8 kf[NT], qf[NT];
 #pragma unroll
                 for (int rt = 0; rt < NT; ++rt) {
-                    kf[rt] = ld_perm8(&s.K[buf][16 * rt + n][0], ss, h);
-                    qf[rt] = ld_perm8(&s.Q[buf][16 * rt + n][0], ss, h);
+                    kf[rt] = *reinterpret_cast<const bf16x8*>(&s.K[buf][16 * rt + n][32 * ss + 8 * h]);
+                    qf[rt] = *reinterpret_cast<const bf16x8*>(&s.Q[buf][16 * rt + n][32 * ss + 8 * h]);
                 }
 #pragma unroll
                 for (int rt = 0; rt < NT; ++rt) X[rt] = mfma_bf16(kf[rt], shi, X[rt]);
