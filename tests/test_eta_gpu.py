@@ -117,3 +117,29 @@ def test_null_eta_is_the_plain_entry():
     # diag(eta) V - diag(beta exp g) K S^T: same values up to rounding
     assert rel_err(O2.cpu().numpy(), O0.cpu().numpy()) < 1e-4
     assert rel_err(S2.cpu().numpy(), S0.cpu().numpy()) < 1e-4
+
+
+def test_random_eta_two_scan_waves_ragged():
+    """Random eta on a head count that runs two scan waves (values staged in
+    LDS), ragged T, sampled heads against the oracle."""
+    x = make_random(4, 16, 200, 128, 128, seed=23, s0_std=0.05)
+    g = torch.Generator().manual_seed(23)
+    eta = 1.5 * torch.rand(x["beta"].shape, generator=g)
+    say("case: random eta, B4 H16 T200 d128 (two scan waves, sampled heads)")
+    d = to_dev(x)
+    O, S = gdn.gdn_chunk_fwd_eta(d["q"], d["k"], d["v"], d["alpha"], d["beta"], eta.cuda(),
+                                 d["S0"], chunk_size=64)
+    torch.cuda.synchronize()
+    heads = [(0, 0), (2, 5), (3, 15)]
+    Os, Ss = [], []
+    for b, h in heads:
+        pick = lambda t: None if t is None else t[b:b + 1, h:h + 1]
+        Or, Sr = oracle.recurrent(pick(x["q"]), pick(x["k"]), pick(x["v"]), pick(x["alpha"]),
+                                  pick(x["beta"]), S0=pick(x["S0"]), eta=pick(eta))
+        Os.append(Or[0, 0])
+        Ss.append(Sr[0, 0])
+    Og = np.stack([O[b, h].cpu().numpy() for b, h in heads])
+    Sg = np.stack([S[b, h].cpu().numpy() for b, h in heads])
+    eo, es = rel_err(Og, np.stack(Os)), rel_err(Sg, np.stack(Ss))
+    say(f"  O {eo:.3e}  S {es:.3e}")
+    assert eo < TOL["bf16"] and es < TOL["bf16"]

@@ -107,6 +107,29 @@ F32_SHAPES = [
 ]
 
 
+# Head counts large enough that the kernel runs two or four scan waves per
+# workgroup (the launch picks four when B*H*d_v/64 >= 256, else two when
+# B*H*d_v/32 >= 256); with one or two the values are staged through LDS by a
+# prep wave, with four the scan waves load them.  Ragged T in every case;
+# sampled heads include the first and the last workgroups.
+WAVE_SHAPES = [
+    # (B, H, T, dk, dv, C)
+    (4, 16, 333, 128, 128, 64),   # two scan waves
+    (4, 16, 97, 64, 128, 32),     # two scan waves, d_k 64, 32-token chunks
+    (8, 32, 150, 64, 64, 64),     # four scan waves
+    (16, 16, 97, 128, 128, 32),   # four scan waves, 32-token chunks
+]
+
+
+@pytest.mark.parametrize("B,H,T,dk,dv,C", WAVE_SHAPES)
+def test_scan_wave_counts_ragged(B, H, T, dk, dv, C):
+    x = make_random(B, H, T, dk, dv, dtype="bf16", chunk=C, seed=T + B, s0_std=0.02)
+    say(f"case: bf16 B{B} H{H} T{T} dk{dk} dv{dv} C{C} (sampled heads)")
+    O, S = run_gpu(x, C)
+    heads = [(0, 0), (B // 2, H // 3), (B - 1, H - 1)]
+    check(x, O, S, heads=heads, label=f"B{B} H{H} T{T} dk{dk} dv{dv} C{C}")
+
+
 @pytest.mark.parametrize("B,H,T,dk,dv,C", F32_SHAPES)
 def test_f32_shapes(B, H, T, dk, dv, C):
     x = make_random(B, H, T, dk, dv, dtype="f32", chunk=C, seed=3 * T + dv, s0_std=0.05,
