@@ -57,7 +57,7 @@ __device__ __forceinline__ float group_sum(float x) {
     return x;
 }
 
-constexpr int kRecThreads = 256;
+constexpr int kRecThreads = 128;
 
 // Rows per lane group: each group keeps R rows (RPB / R apart), so k_t and
 // q_t are loaded once per token for R rows and R times the state bytes are
