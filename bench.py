@@ -62,6 +62,19 @@ def measured_traffic(kernel: str, workload: str):
     return rec.get("hbm_bytes_per_launch")
 
 
+def cpu_model() -> str:
+    """The host CPU's model name (first processor in /proc/cpuinfo)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
 def cpu_baseline(x, w, target_seconds=10.0):
     """Time the fp64 oracle on this host over a bounded sample of the same
     workload: whole (b, h) sequences (all of them when the workload is small
@@ -94,6 +107,7 @@ def cpu_baseline(x, w, target_seconds=10.0):
     # tokens/s on the metric's scale: B*T positions of all H heads per step
     tok_s = head_tokens / dt / w.H
     return {"value": tok_s, "unit": "tokens/s", "cores": nthreads, "kind": "oracle",
+            "cpu_model": cpu_model(),
             "sample": f"{nsel} of {heads_total} (b,h) sequences at full T={w.T}, "
                       f"{reps} pass(es), fp64 recurrence",
             "seconds": dt}

@@ -34,8 +34,8 @@ from dataclasses import dataclass
 
 import torch
 
-__all__ = ["Workload", "WORKLOADS", "make_inputs", "make_random", "algorithmic_bytes",
-           "algorithmic_flops"]
+__all__ = ["Workload", "WORKLOADS", "make_inputs", "make_random", "chunk_scaled_alpha",
+           "algorithmic_bytes", "algorithmic_flops"]
 
 
 @dataclass(frozen=True)
@@ -134,6 +134,21 @@ def make_random(B, H, T, dk, dv, dtype="bf16", chunk=64, seed=0, alpha_scale=0.0
     w = Workload("custom", B, H, T, dk, dv, chunk, dtype, beta_kind=beta_kind,
                  alpha_kind=alpha_kind, alpha_scale=alpha_scale, s0_std=s0_std)
     return make_inputs(w, seed)
+
+
+def chunk_scaled_alpha(B, H, T, chunk, scales, seed=0) -> torch.Tensor:
+    """Gates alpha = exp(-softplus(N(0,1)) * s) whose scale s changes from
+    chunk to chunk, cycling through ``scales`` (chunk c of every sequence
+    uses scales[c % len(scales)]).  Large scales give strong gates (alpha
+    near 0.04 at s = 4), so that one chunk's decay spans hundreds of binary
+    orders of magnitude; mixing scales puts weakly and strongly gated chunks
+    side by side in one sequence."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(seed)
+    n = torch.randn(B, H, T, generator=g)
+    idx = (torch.arange(T) // chunk) % len(scales)
+    s = torch.tensor([float(v) for v in scales])[idx]
+    return torch.exp(-torch.nn.functional.softplus(n) * s).float().contiguous()
 
 
 def algorithmic_bytes(w: Workload, o_bytes: int = 4, with_alpha: bool | None = None,

@@ -29,9 +29,21 @@ def to_dev(x: dict, device="cuda") -> dict:
     return out
 
 
+def nan_outputs(x: dict, o_dtype=torch.float32, device="cuda"):
+    """O and S_final buffers pre-filled with NaN: an element the kernel never
+    writes stays NaN and fails the finiteness check."""
+    B, H, T, dk = x["q"].shape
+    dv = x["v"].shape[-1]
+    O = torch.full((B, H, T, dv), float("nan"), dtype=o_dtype, device=device)
+    S = torch.full((B, H, dv, dk), float("nan"), dtype=torch.float32, device=device)
+    return O, S
+
+
 def run_gpu(x: dict, chunk: int, o_dtype=torch.float32, S0=None, **kw):
     d = to_dev(x)
     s0 = d["S0"] if S0 is None else S0
+    if "O" not in kw and "S_final" not in kw:
+        kw["O"], kw["S_final"] = nan_outputs(x, o_dtype)
     O, S = gdn.gdn_chunk_fwd(d["q"], d["k"], d["v"], d["alpha"], d["beta"], s0,
                              chunk_size=chunk, o_dtype=o_dtype, **kw)
     torch.cuda.synchronize()
@@ -60,6 +72,17 @@ def rel_err(x, ref) -> float:
     if denom == 0:
         return float(np.abs(x).max())
     return float(np.abs(x - ref).max() / denom)
+
+
+def elem_err(x, ref) -> float:
+    """Elementwise diagnostic (reported, not gated): max_i |x_i - ref_i| /
+    max(|ref_i|, 1e-3 max_j |ref_j|)."""
+    x = np.asarray(x, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    floor = 1e-3 * np.abs(ref).max()
+    if floor == 0:
+        return float(np.abs(x).max())
+    return float((np.abs(x - ref) / np.maximum(np.abs(ref), floor)).max())
 
 
 def gpu_heads(t: torch.Tensor, heads):
