@@ -15,7 +15,8 @@ import ctypes
 
 from ._lib import (EXPORTS, GDN_BF16, GDN_F32, GdnError, GdnShape, check, load)
 
-__all__ = ["gdn_chunk_fwd", "gdn_chunk_fwd_eta", "gdn_chunk_prep", "gdn_chunk_fwd_workspace_bytes",
+__all__ = ["gdn_chunk_fwd", "gdn_chunk_fwd_eta", "gdn_chunk_fwd_precise", "gdn_chunk_fwd_stages",
+           "gdn_chunk_prep", "gdn_chunk_fwd_workspace_bytes",
            "gdn_recurrent_fwd", "gdn_recurrent_fwd_eta",
            "gdn_status_string", "gdn_last_error", "gdn_version", "GdnError", "GdnShape",
            "EXPORTS"]
@@ -72,15 +73,8 @@ def gdn_chunk_fwd_workspace_bytes(shape: GdnShape) -> int:
     return int(n)
 
 
-def gdn_chunk_fwd(q, k, v, alpha, beta, S0=None, chunk_size: int = 64, o_dtype=None,
-                  O=None, S_final=None, stream=None, eta=None):
-    """Forward pass on the GPU.  q, k [B,H,T,d_k] and v [B,H,T,d_v] (bf16 or
-    fp32, one dtype); alpha (or None = 1), beta [B,H,T] fp32; S0 [B,H,d_v,d_k]
-    fp32 or None (zero).  Returns (O [B,H,T,d_v] in o_dtype (fp32 default),
-    S_final [B,H,d_v,d_k] fp32).  O / S_final may be passed in (S_final may
-    be S0: in-place state update).  Runs on the current stream, asynchronously.
-    eta [B,H,T] fp32, if given, is a separate write strength (the C entry
-    gdn_chunk_fwd_eta); None means eta = beta."""
+def _chunk_call(entry, q, k, v, alpha, beta, S0, chunk_size, o_dtype, O, S_final, stream, eta,
+                extra=()):
     torch = _torch()
     lib = load()
     B, H, T, dk = q.shape
@@ -103,18 +97,67 @@ def gdn_chunk_fwd(q, k, v, alpha, beta, S0=None, chunk_size: int = 64, o_dtype=N
         S_final = torch.empty((B, H, dv, dk), dtype=torch.float32, device=dev)
     _check_tensor("S_final", S_final, (B, H, dv, dk), torch.float32, dev)
     shape = make_shape(B, H, T, dk, dv, chunk_size, q.dtype, o_dtype)
-    ws_bytes = gdn_chunk_fwd_workspace_bytes(shape)
-    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None
-    if eta is None:
-        st = lib.gdn_chunk_fwd(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha),
-                               _ptr(beta), _ptr(S0), _ptr(O), _ptr(S_final), _ptr(ws), ws_bytes,
-                               _stream_handle(dev, stream))
+    hs = _stream_handle(dev, stream)
+    if entry == "fast":
+        ws_bytes = gdn_chunk_fwd_workspace_bytes(shape)
+        ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None
+        if eta is None:
+            st = lib.gdn_chunk_fwd(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha),
+                                   _ptr(beta), _ptr(S0), _ptr(O), _ptr(S_final), _ptr(ws),
+                                   ws_bytes, hs)
+        else:
+            st = lib.gdn_chunk_fwd_eta(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v),
+                                       _ptr(alpha), _ptr(beta), _ptr(eta), _ptr(S0), _ptr(O),
+                                       _ptr(S_final), _ptr(ws), ws_bytes, hs)
+    elif entry == "precise":
+        st = lib.gdn_chunk_fwd_precise(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v),
+                                       _ptr(alpha), _ptr(beta), _ptr(eta), _ptr(S0), _ptr(O),
+                                       _ptr(S_final), hs)
     else:
-        st = lib.gdn_chunk_fwd_eta(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha),
-                                   _ptr(beta), _ptr(eta), _ptr(S0), _ptr(O), _ptr(S_final),
-                                   _ptr(ws), ws_bytes, _stream_handle(dev, stream))
+        T_out, Vp_out = extra
+        st = lib.gdn_chunk_fwd_stages(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v),
+                                      _ptr(alpha), _ptr(beta), _ptr(eta), _ptr(S0), _ptr(O),
+                                      _ptr(S_final), _ptr(T_out), _ptr(Vp_out), hs)
     check(st)
     return O, S_final
+
+
+def gdn_chunk_fwd(q, k, v, alpha, beta, S0=None, chunk_size: int = 64, o_dtype=None,
+                  O=None, S_final=None, stream=None, eta=None):
+    """Forward pass on the GPU.  q, k [B,H,T,d_k] and v [B,H,T,d_v] (bf16 or
+    fp32, one dtype); alpha (or None = 1), beta [B,H,T] fp32; S0 [B,H,d_v,d_k]
+    fp32 or None (zero).  Returns (O [B,H,T,d_v] in o_dtype (fp32 default),
+    S_final [B,H,d_v,d_k] fp32).  O / S_final may be passed in (S_final may
+    be S0: in-place state update).  Runs on the current stream, asynchronously.
+    eta [B,H,T] fp32, if given, is a separate write strength (the C entry
+    gdn_chunk_fwd_eta); None means eta = beta.  bf16 inputs take the fp16-
+    operand kernel (gdn_chunk_fwd_precise is the split-bf16 alternative)."""
+    return _chunk_call("fast", q, k, v, alpha, beta, S0, chunk_size, o_dtype, O, S_final,
+                       stream, eta)
+
+
+def gdn_chunk_fwd_precise(q, k, v, alpha, beta, S0=None, chunk_size: int = 64, o_dtype=None,
+                          O=None, S_final=None, stream=None, eta=None):
+    """The same pass through the split-bf16 kernels (every derived MFMA
+    operand as a bf16 hi + lo pair: errors near 1e-5 whatever the gates)."""
+    return _chunk_call("precise", q, k, v, alpha, beta, S0, chunk_size, o_dtype, O, S_final,
+                       stream, eta)
+
+
+def gdn_chunk_fwd_stages(q, k, v, alpha, beta, S0=None, chunk_size: int = 64, o_dtype=None,
+                         eta=None, stream=None):
+    """The default bf16 pass with its intermediates written out: returns
+    (O, S_final, T [B,H,NT,C,C] = (I - A)^{-1} per chunk, V' [B,H,T,d_v] the
+    pseudo-values), fp32."""
+    torch = _torch()
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    nt = (T + chunk_size - 1) // chunk_size
+    T_out = torch.zeros((B, H, nt, chunk_size, chunk_size), dtype=torch.float32, device=q.device)
+    Vp_out = torch.zeros((B, H, T, dv), dtype=torch.float32, device=q.device)
+    O, S = _chunk_call("stages", q, k, v, alpha, beta, S0, chunk_size, o_dtype, None, None,
+                       stream, eta, extra=(T_out, Vp_out))
+    return O, S, T_out, Vp_out
 
 
 def gdn_recurrent_fwd(q, k, v, alpha, beta, S0=None, o_dtype=None, O=None, S_final=None,

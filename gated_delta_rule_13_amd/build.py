@@ -1,9 +1,12 @@
 """Build the gfx950 HIP library ``libgdn.so`` in-tree with hipcc.
 
-    python -m gated_delta_rule_13_amd.build
+    python -m gated_delta_rule_13_amd.build [-v]
 
 All device code is compiled for gfx950 only, with packed-fp32 instruction
 selection disabled (``-Xclang -target-feature -Xclang -packed-fp32-ops``).
+Each kernel family is its own translation unit (the fp16-operand kernel once
+per (chunk, d_k) pair), compiled in parallel into objects under
+``_build/`` and linked into one shared library.
 """
 from __future__ import annotations
 
@@ -11,14 +14,19 @@ import os
 import shutil
 import subprocess
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
+BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libgdn.so")
-SOURCES = [os.path.join(CSRC, "gdn_api.hip")]
 ARCH = "gfx950"
+
+# (chunk, d_k) pairs of the fp16-operand kernel; d_k 256 only up to 32-token
+# chunks (the double-buffered key and query tiles of 64 would not fit in LDS)
+FAST_PAIRS = [(c, d) for c in (16, 32, 64) for d in (32, 64, 96, 128)] + [(16, 256), (32, 256)]
 
 
 def hipcc() -> str:
@@ -28,25 +36,55 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
-def compile_command(out: str) -> list[str]:
-    return [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+def common_flags() -> list[str]:
+    return [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-            "-Wall", "-Wno-unused-function",
-            f"-I{INCLUDE}", f"-I{CSRC}", *SOURCES, "-o", out]
+            "-Wall", "-Wno-unused-function", f"-I{INCLUDE}", f"-I{CSRC}"]
 
 
-def build(verbose: bool = False) -> str:
-    tmp = LIB + f".tmp{os.getpid()}"
-    cmd = compile_command(tmp)
-    if verbose:
-        print(" ".join(cmd), flush=True)
+def units() -> list[tuple[str, str, list[str]]]:
+    """(object name, source, extra flags) of every translation unit."""
+    out = [("gdn_api.o", "gdn_api.hip", []),
+           ("gdn_inst_pipe.o", "gdn_inst_pipe.hip", []),
+           ("gdn_inst_generic.o", "gdn_inst_generic.hip", []),
+           ("gdn_inst_rec.o", "gdn_inst_rec.hip", [])]
+    for c, d in FAST_PAIRS:
+        out.append((f"gdn_inst_fast_c{c}_d{d}.o", "gdn_inst_fast.hip", [f"-DGDN_C={c}", f"-DGDN_DK={d}"]))
+    return out
+
+
+NOISE = "is not a recognized feature for this target"
+
+
+def _run(cmd: list[str]) -> tuple[int, str]:
     res = subprocess.run(cmd, capture_output=True, text=True)
-    noise = "is not a recognized feature for this target"
-    err = "\n".join(l for l in res.stderr.splitlines() if noise not in l)
-    if res.returncode != 0:
-        raise RuntimeError("HIP build failed:\n" + " ".join(cmd) + "\n" + err)
-    if verbose and err.strip():
-        print(err)
+    err = "\n".join(l for l in res.stderr.splitlines() if NOISE not in l)
+    return res.returncode, err
+
+
+def build(verbose: bool = False, jobs: int | None = None) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    jobs = jobs or min(16, os.cpu_count() or 4)
+    cmds = []
+    objs = []
+    for obj, src, extra in units():
+        o = os.path.join(BUILD, obj)
+        objs.append(o)
+        cmds.append([hipcc(), *common_flags(), *extra, "-c", os.path.join(CSRC, src), "-o", o])
+    with ThreadPoolExecutor(max_workers=jobs) as ex:
+        results = list(ex.map(_run, cmds))
+    for cmd, (rc, err) in zip(cmds, results):
+        if rc != 0:
+            raise RuntimeError("HIP build failed:\n" + " ".join(cmd) + "\n" + err)
+        if verbose:
+            print(" ".join(cmd), flush=True)
+            if err.strip():
+                print(err)
+    tmp = LIB + f".tmp{os.getpid()}"
+    link = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
+    rc, err = _run(link)
+    if rc != 0:
+        raise RuntimeError("HIP link failed:\n" + " ".join(link) + "\n" + err)
     os.replace(tmp, LIB)
     return LIB
 

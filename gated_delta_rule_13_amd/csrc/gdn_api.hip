@@ -7,9 +7,7 @@
 #include <string>
 
 #include "gdn.h"
-#include "gdn_kernels.h"
-#include "gdn_pipe.h"
-#include "gdn_recurrent.h"
+#include "gdn_launch.h"
 
 namespace {
 
@@ -22,16 +20,21 @@ gdn_status fail(gdn_status st, const std::string& msg) {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-// Built shapes.  bf16: C in {32, 64}, d_k in {32, 64, 128};
-// f32: C in {16, 32, 64}, d_k in {16, 32, 64}.  d_v: multiple of 16.
+// Built shapes of the default (fp16-operand) path for bf16 inputs.
+bool fast_pair(int C, int dk) {
+    if (C != 16 && C != 32 && C != 64) return false;
+    if (dk == 32 || dk == 64 || dk == 96 || dk == 128) return true;
+    return dk == 256 && C <= 32;
+}
+
+// Shapes some kernel covers.  bf16: the fast path's pairs (plus C in
+// {32, 64} with d_k 32 via the generic kernel); f32: C in {16, 32, 64},
+// d_k in {16, 32, 64}.  d_v: multiple of 16 in [16, 1024].
 bool supported(const gdn_shape& s, std::string* why) {
     if (s.qkv_dtype == GDN_BF16) {
-        if (s.chunk_size != 32 && s.chunk_size != 64) {
-            *why = "bf16 inputs need chunk_size 32 or 64";
-            return false;
-        }
-        if (s.d_k != 32 && s.d_k != 64 && s.d_k != 128) {
-            *why = "bf16 inputs need d_k in {32, 64, 128}";
+        if (!fast_pair(s.chunk_size, s.d_k)) {
+            *why = "bf16 inputs need chunk_size in {16, 32, 64} and d_k in {32, 64, 96, 128} "
+                   "(d_k 256 with chunk_size <= 32)";
             return false;
         }
     } else {
@@ -64,11 +67,17 @@ gdn_status validate_shape(const gdn_shape* s) {
     if (elems > 4.0e18L) return fail(GDN_ERR_BAD_SHAPE, "tensor too large");
     std::string why;
     if (!supported(*s, &why)) return fail(GDN_ERR_UNSUPPORTED, why);
+    // the fused kernels address one head's rows through 32-bit buffer
+    // offsets: one head's largest tensor (fp32 output) must stay below 2 GiB
+    const size_t head_bytes = (size_t)s->T * (size_t)(s->d_k > s->d_v ? s->d_k : s->d_v) * 4;
+    if (head_bytes >= ((size_t)1 << 31))
+        return fail(GDN_ERR_UNSUPPORTED, "one head's tensors must stay below 2 GiB (T too long)");
     return GDN_OK;
 }
 
-// Waves per workgroup (16 value columns each): the largest of 4, 2, 1 that
-// divides d_v / 16 and still gives at least one workgroup per compute unit.
+// Waves per workgroup of the generic kernel (16 value columns each): the
+// largest of 4, 2, 1 that divides d_v / 16 and still gives at least one
+// workgroup per compute unit.
 int choose_waves(const gdn_shape& s) {
     const int cols16 = s.d_v / 16;
     const long heads = (long)s.B * s.H;
@@ -81,39 +90,9 @@ int choose_waves(const gdn_shape& s) {
     return best;
 }
 
-template <int C, int DK, int NW, bool BF>
-void launch_fwd(const gdn::FwdParams& p, long nblocks, hipStream_t st) {
-    hipLaunchKernelGGL((gdn::gdn_fwd_kernel<C, DK, NW, BF>), dim3((unsigned)nblocks),
-                       dim3(NW * 64), 0, st, p);
-}
-template <int C, int DK, int NW, bool BF>
-void launch_prep(const gdn::FwdParams& p, long nblocks, hipStream_t st) {
-    hipLaunchKernelGGL((gdn::gdn_prep_kernel<C, DK, NW, BF>), dim3((unsigned)nblocks),
-                       dim3(NW * 64), 0, st, p);
-}
-
-using Launcher = void (*)(const gdn::FwdParams&, long, hipStream_t);
-
-template <int C, int DK, int NS>
-void launch_pipe(const gdn::FwdParams& p, long nblocks, hipStream_t st) {
-    if (p.eta)
-        hipLaunchKernelGGL((gdn::gdn_fwd_pipe_kernel<C, DK, NS, true>), dim3((unsigned)nblocks),
-                           dim3((NS + gdn::kPrepWaves) * 64), 0, st, p);
-    else
-        hipLaunchKernelGGL((gdn::gdn_fwd_pipe_kernel<C, DK, NS, false>), dim3((unsigned)nblocks),
-                           dim3((NS + gdn::kPrepWaves) * 64), 0, st, p);
-}
-
-// Pipelined kernel: bf16 inputs, C in {32, 64}, d_k in {64, 128}.  NS scan
-// waves of 16 value columns each per workgroup: the largest of 4, 2, 1 that
-// divides d_v / 16 and still gives one workgroup per compute unit (256).
-// The pipelined kernel addresses one head's rows through 32-bit buffer
-// offsets, so one head's largest tensor (fp32 output) must stay below 2 GiB.
-bool pipe_supported(const gdn_shape& s) {
-    const size_t head_bytes = (size_t)s.T * (size_t)(s.d_k > s.d_v ? s.d_k : s.d_v) * 4;
-    return s.qkv_dtype == GDN_BF16 && (s.chunk_size == 32 || s.chunk_size == 64) &&
-           (s.d_k == 64 || s.d_k == 128) && head_bytes < ((size_t)1 << 31);
-}
+// Scan waves per workgroup of the pipelined kernels (16 value columns each):
+// the largest of 4, 2 that divides d_v / 16 and still gives one workgroup per
+// compute unit (256), else 1.
 int choose_scan_waves(const gdn_shape& s) {
     const long heads = (long)s.B * s.H;
     const int cols16 = s.d_v / 16;
@@ -121,81 +100,109 @@ int choose_scan_waves(const gdn_shape& s) {
         if (cols16 % ns == 0 && heads * (cols16 / ns) >= 256) return ns;
     return 1;
 }
-Launcher pick_pipe(const gdn_shape& s, int ns) {
-    const int C = s.chunk_size, DK = s.d_k;
-#define GDN_PIPE(CC, KK)                                                        \
-    if (C == CC && DK == KK)                                                    \
-        return ns == 4 ? launch_pipe<CC, KK, 4>                                 \
-                       : ns == 2 ? launch_pipe<CC, KK, 2> : launch_pipe<CC, KK, 1>;
-    GDN_PIPE(64, 128)
-    GDN_PIPE(64, 64)
-    GDN_PIPE(32, 128)
-    GDN_PIPE(32, 64)
-#undef GDN_PIPE
-    return nullptr;
-}
 
-template <int C, int DK, bool BF>
-Launcher pick_nw(int nw, bool prep) {
-    switch (nw) {
-        case 1: return prep ? launch_prep<C, DK, 1, BF> : launch_fwd<C, DK, 1, BF>;
-        case 2: return prep ? launch_prep<C, DK, 2, BF> : launch_fwd<C, DK, 2, BF>;
-        default: return prep ? launch_prep<C, DK, 4, BF> : launch_fwd<C, DK, 4, BF>;
-    }
-}
-
-Launcher pick(const gdn_shape& s, int nw, bool prep) {
-    const int C = s.chunk_size, DK = s.d_k;
-    if (s.qkv_dtype == GDN_BF16) {
-        if (C == 64 && DK == 128) return pick_nw<64, 128, true>(nw, prep);
-        if (C == 64 && DK == 64) return pick_nw<64, 64, true>(nw, prep);
-        if (C == 64 && DK == 32) return pick_nw<64, 32, true>(nw, prep);
-        if (C == 32 && DK == 128) return pick_nw<32, 128, true>(nw, prep);
-        if (C == 32 && DK == 64) return pick_nw<32, 64, true>(nw, prep);
-        if (C == 32 && DK == 32) return pick_nw<32, 32, true>(nw, prep);
-    } else {
-        if (C == 64 && DK == 64) return pick_nw<64, 64, false>(nw, prep);
-        if (C == 64 && DK == 32) return pick_nw<64, 32, false>(nw, prep);
-        if (C == 64 && DK == 16) return pick_nw<64, 16, false>(nw, prep);
-        if (C == 32 && DK == 64) return pick_nw<32, 64, false>(nw, prep);
-        if (C == 32 && DK == 32) return pick_nw<32, 32, false>(nw, prep);
-        if (C == 32 && DK == 16) return pick_nw<32, 16, false>(nw, prep);
-        if (C == 16 && DK == 64) return pick_nw<16, 64, false>(nw, prep);
-        if (C == 16 && DK == 32) return pick_nw<16, 32, false>(nw, prep);
-        if (C == 16 && DK == 16) return pick_nw<16, 16, false>(nw, prep);
-    }
-    return nullptr;
-}
-
-using RecLauncher = void (*)(const gdn::RecParams&, long, hipStream_t);
-
-template <int DK, bool BF>
-void launch_rec(const gdn::RecParams& p, long nblocks, hipStream_t st) {
-    hipLaunchKernelGGL((gdn::gdn_recurrent_kernel<DK, BF>), dim3((unsigned)nblocks),
-                       dim3(gdn::kRecThreads), 0, st, p);
-}
-
-RecLauncher pick_rec(int dk, bool bf, int* rows_per_block) {
-#define GDN_REC(D)                                                               \
-    if (dk == D) {                                                               \
-        *rows_per_block = gdn::kRecRows * (gdn::kRecThreads / 64) * (64 / gdn::rec_lanes_per_row(D)); \
-        return bf ? launch_rec<D, true> : launch_rec<D, false>;                  \
-    }
-    GDN_REC(16)
-    GDN_REC(32)
-    GDN_REC(64)
-    GDN_REC(96)
-    GDN_REC(128)
-    GDN_REC(192)
-    GDN_REC(256)
-#undef GDN_REC
-    return nullptr;
+bool pipe_shape(const gdn_shape& s) {
+    return s.qkv_dtype == GDN_BF16 && (s.chunk_size == 32 || s.chunk_size == 64) &&
+           (s.d_k == 64 || s.d_k == 128);
 }
 
 gdn_status check_launch() {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(GDN_ERR_HIP, hipGetErrorString(e));
     return GDN_OK;
+}
+
+}  // namespace
+
+namespace gdn {
+FwdLauncher fast_launcher(int C, int dk, int ns, bool eta) {
+#define GDN_FAST_PICK(CC, KK) \
+    if (C == CC && dk == KK) return fast_launcher_c##CC##_d##KK(ns, eta);
+    GDN_FAST_PICK(16, 32)
+    GDN_FAST_PICK(16, 64)
+    GDN_FAST_PICK(16, 96)
+    GDN_FAST_PICK(16, 128)
+    GDN_FAST_PICK(16, 256)
+    GDN_FAST_PICK(32, 32)
+    GDN_FAST_PICK(32, 64)
+    GDN_FAST_PICK(32, 96)
+    GDN_FAST_PICK(32, 128)
+    GDN_FAST_PICK(32, 256)
+    GDN_FAST_PICK(64, 32)
+    GDN_FAST_PICK(64, 64)
+    GDN_FAST_PICK(64, 96)
+    GDN_FAST_PICK(64, 128)
+#undef GDN_FAST_PICK
+    return nullptr;
+}
+}  // namespace gdn
+
+namespace {
+
+enum class Path { kFast, kPrecise };
+
+struct ChunkArgs {
+    const void *q, *k, *v;
+    const float *alpha, *beta, *eta, *S0;
+    void* O;
+    float* S_final;
+    float* dbg_T;
+    float* dbg_V;
+};
+
+gdn_status run_chunk(const gdn_shape* s, const ChunkArgs& a, Path path, void* stream) {
+    g_last_error.clear();
+    gdn_status st = validate_shape(s);
+    if (st != GDN_OK) return st;
+    if (!a.q || !a.k || !a.v || !a.beta || !a.O || !a.S_final)
+        return fail(GDN_ERR_NULL_ARG, "q, k, v, beta, O and S_final are required");
+    if (!aligned16(a.q) || !aligned16(a.k) || !aligned16(a.v) || !aligned16(a.O) ||
+        !aligned16(a.S_final) || (a.S0 && !aligned16(a.S0)) || !aligned16(a.beta) ||
+        (a.alpha && !aligned16(a.alpha)) || (a.eta && !aligned16(a.eta)) ||
+        (a.dbg_T && !aligned16(a.dbg_T)) || (a.dbg_V && !aligned16(a.dbg_V)))
+        return fail(GDN_ERR_UNSUPPORTED, "tensor pointers must be 16-byte aligned");
+    const bool bf = s->qkv_dtype == GDN_BF16;
+    gdn::FwdLauncher launch = nullptr;
+    int nw = 1;
+    bool pipelined = false;
+    if (bf && path == Path::kFast) {
+        nw = choose_scan_waves(*s);
+        launch = gdn::fast_launcher(s->chunk_size, s->d_k, nw, a.eta != nullptr);
+        pipelined = true;
+    } else if (bf && pipe_shape(*s)) {
+        nw = choose_scan_waves(*s);
+        launch = gdn::pipe_launcher(s->chunk_size, s->d_k, nw, a.eta != nullptr);
+        pipelined = true;
+    } else {
+        nw = choose_waves(*s);
+        launch = gdn::generic_launcher(s->chunk_size, s->d_k, nw, bf, false);
+    }
+    if (!launch) return fail(GDN_ERR_UNSUPPORTED, "shape not built for this path");
+    if ((a.dbg_T || a.dbg_V) && !(bf && path == Path::kFast))
+        return fail(GDN_ERR_UNSUPPORTED, "stage outputs exist for the fast bf16 path only");
+    gdn::FwdParams p{};
+    p.q = a.q;
+    p.k = a.k;
+    p.v = a.v;
+    p.alpha = a.alpha;
+    p.beta = a.beta;
+    p.eta = a.eta;
+    p.S0 = a.S0;
+    p.O = a.O;
+    p.S_final = a.S_final;
+    p.dbg_T = a.dbg_T;
+    p.dbg_V = a.dbg_V;
+    p.B = s->B;
+    p.H = s->H;
+    p.T = s->T;
+    p.dv = s->d_v;
+    p.n_tiles = s->d_v / (16 * nw);
+    p.o_bf16 = s->o_dtype == GDN_BF16;
+    p.xcd_groups = pipelined && ((long)s->B * s->H) % 8 == 0;
+    const long nblocks = (long)s->B * s->H * p.n_tiles;
+    if (nblocks > 0x7fffffffL) return fail(GDN_ERR_BAD_SHAPE, "grid too large");
+    launch(p, nblocks, reinterpret_cast<hipStream_t>(stream));
+    return check_launch();
 }
 
 }  // namespace
@@ -220,40 +227,27 @@ gdn_status gdn_chunk_fwd_eta(const gdn_shape* s, const void* q, const void* k, c
                              size_t workspace_bytes, void* stream) {
     (void)workspace;
     (void)workspace_bytes;
-    g_last_error.clear();
-    gdn_status st = validate_shape(s);
-    if (st != GDN_OK) return st;
-    if (!q || !k || !v || !beta || !O || !S_final)
-        return fail(GDN_ERR_NULL_ARG, "q, k, v, beta, O and S_final are required");
-    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(O) || !aligned16(S_final) ||
-        (S0 && !aligned16(S0)) || !aligned16(beta) || (alpha && !aligned16(alpha)) ||
-        (eta && !aligned16(eta)))
-        return fail(GDN_ERR_UNSUPPORTED, "tensor pointers must be 16-byte aligned");
-    const bool piped = pipe_supported(*s);
-    const int nw = piped ? choose_scan_waves(*s) : choose_waves(*s);
-    const Launcher launch = piped ? pick_pipe(*s, nw) : pick(*s, nw, false);
-    if (!launch) return fail(GDN_ERR_UNSUPPORTED, "shape not built");
-    gdn::FwdParams p{};
-    p.q = q;
-    p.k = k;
-    p.v = v;
-    p.alpha = alpha;
-    p.beta = beta;
-    p.eta = eta;
-    p.S0 = S0;
-    p.O = O;
-    p.S_final = S_final;
-    p.B = s->B;
-    p.H = s->H;
-    p.T = s->T;
-    p.dv = s->d_v;
-    p.n_tiles = s->d_v / (16 * nw);
-    p.o_bf16 = s->o_dtype == GDN_BF16;
-    p.xcd_groups = piped && ((long)s->B * s->H) % 8 == 0;
-    const long nblocks = (long)s->B * s->H * p.n_tiles;
-    if (nblocks > 0x7fffffffL) return fail(GDN_ERR_BAD_SHAPE, "grid too large");
-    launch(p, nblocks, reinterpret_cast<hipStream_t>(stream));
-    return check_launch();
+    return run_chunk(s, ChunkArgs{q, k, v, alpha, beta, eta, S0, O, S_final, nullptr, nullptr},
+                     Path::kFast, stream);
+}
+
+gdn_status gdn_chunk_fwd_precise(const gdn_shape* s, const void* q, const void* k, const void* v,
+                                 const float* alpha, const float* beta, const float* eta,
+                                 const float* S0, void* O, float* S_final, void* stream) {
+    return run_chunk(s, ChunkArgs{q, k, v, alpha, beta, eta, S0, O, S_final, nullptr, nullptr},
+                     Path::kPrecise, stream);
+}
+
+gdn_status gdn_chunk_fwd_stages(const gdn_shape* s, const void* q, const void* k, const void* v,
+                                const float* alpha, const float* beta, const float* eta,
+                                const float* S0, void* O, float* S_final, float* T_out,
+                                float* Vp_out, void* stream) {
+    if (s && s->qkv_dtype != GDN_BF16) {
+        g_last_error = "stage outputs exist for bf16 inputs only";
+        return GDN_ERR_UNSUPPORTED;
+    }
+    return run_chunk(s, ChunkArgs{q, k, v, alpha, beta, eta, S0, O, S_final, T_out, Vp_out},
+                     Path::kFast, stream);
 }
 
 gdn_status gdn_chunk_prep(const gdn_shape* s, const void* k, const void* v, const float* alpha,
@@ -269,8 +263,9 @@ gdn_status gdn_chunk_prep(const gdn_shape* s, const void* k, const void* v, cons
         return fail(GDN_ERR_UNSUPPORTED, "tensor pointers must be 16-byte aligned");
     if (!T_out && !W_out && !U_out) return GDN_OK;
     const int nw = choose_waves(*s);
-    const Launcher launch = pick(*s, nw, true);
-    if (!launch) return fail(GDN_ERR_UNSUPPORTED, "shape not built");
+    const gdn::FwdLauncher launch =
+        gdn::generic_launcher(s->chunk_size, s->d_k, nw, s->qkv_dtype == GDN_BF16, true);
+    if (!launch) return fail(GDN_ERR_UNSUPPORTED, "shape not built for the stage kernel");
     gdn::FwdParams p{};
     p.k = k;
     p.v = v;
@@ -311,7 +306,7 @@ gdn_status gdn_recurrent_fwd_eta(const gdn_shape* s, const void* q, const void* 
     if (elems > 4.0e18L) return fail(GDN_ERR_BAD_SHAPE, "tensor too large");
     if (s->d_v > 65536) return fail(GDN_ERR_UNSUPPORTED, "d_v must be <= 65536");
     int rpb = 0;
-    const RecLauncher launch = pick_rec(s->d_k, s->qkv_dtype == GDN_BF16, &rpb);
+    const gdn::RecLauncher launch = gdn::rec_launcher(s->d_k, s->qkv_dtype == GDN_BF16, &rpb);
     if (!launch) return fail(GDN_ERR_UNSUPPORTED, "d_k must be one of 16, 32, 64, 96, 128, 192, 256");
     if (!q || !k || !v || !beta || !O || !S_final)
         return fail(GDN_ERR_NULL_ARG, "q, k, v, beta, O and S_final are required");
@@ -354,6 +349,6 @@ const char* gdn_status_string(gdn_status st) {
 
 const char* gdn_last_error(void) { return g_last_error.c_str(); }
 
-int32_t gdn_version(void) { return 100; }
+int32_t gdn_version(void) { return 200; }
 
 }  // extern "C"

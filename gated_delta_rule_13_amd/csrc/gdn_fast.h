@@ -1,0 +1,689 @@
+// gdn_fast.h -- fused chunkwise gated delta rule forward pass for bf16
+// inputs on gfx950, with fp16 MFMA operands.
+//
+// Chunk algebra ("从零开始的 GDN 推导": A, then U and W, then the S update and
+// the O update; transposed to the d_v x d_k state of "RNN的复兴03", section 4):
+//   g_r  = sum_{j<=r} log alpha_j                  (chunk-local, kept in base 2)
+//   A_ri = -beta_r exp(g_r - g_i) k_r.k_i (i < r),  T = (I - A)^{-1}
+//   V'   = T diag(beta) (V - diag(exp g) K S^T)      (= U - W S^T, W never formed)
+//   O    = diag(exp g) Q S^T + P V',   P_ri = exp(g_r - g_i) q_r.k_i (i <= r)
+//   S   <- exp(g_last) S + V'^T diag(exp(g_last - g)) K
+// with eta (write strength, "RNN的复兴03" section 1) in place of the first
+// beta of V' when given.
+//
+// T is formed whole, off the serial chain: its 16 x 16 diagonal blocks by
+// substitution ("RNN的复兴03", section 2.3.1, row by row from T = I + T A), and
+// the blocks below the diagonal by block substitution
+//     T_bc = T_bb sum_{c<=k<b} A_bk T_kc
+// on MFMA.  The serial chain over chunks then holds three dense products per
+// chunk: X = K S^T, V' = T Y and the state update, each one MFMA per tile.
+//
+// Precision: every MFMA operand is fp16 (11 significant bits) with fp32
+// accumulation and an fp32 state.  q, k, v arrive as bf16 and convert to
+// fp16 exactly while |x| lies in [2^-14, 65504]; derived operands (the
+// state, T, the pseudo-values, the scores) are rounded to fp16 once per
+// product.  Operand magnitudes must stay below 65504 (the fp16 range).
+//
+// Work is split by role inside the workgroup.  NS "scan" waves own 16 value
+// columns each and that slice of the fp32 state (S^T in MFMA accumulators);
+// four "prep" waves build chunk-local matrices one or two chunks ahead.
+// Iteration i (chunk i on the scan waves) has two phases separated by
+// workgroup barriers:
+//   phase A  scan    X_i = K_i S^T, Z^T_i = S Q_i^T
+//            prep 0  blocks of T_i below the diagonal (T_bb of chunk i and
+//                    its A blocks are from iteration i - 1)
+//            prep 1+ row strips of chunk i + 1: Gram and score tiles formed
+//                    into the diagonal blocks of A (fp32), the blocks below
+//                    them (fp16) and the masked decayed scores P (fp16); the
+//                    keys transposed (for the state update)
+//   phase B  scan    Y, V' = T_i Y, state update, O = diag(exp g) Z + P V'
+//            prep 0  decay vectors of chunk i + 2; diagonal solves of chunk i + 1
+//            prep 1+ keys and queries of chunk i + 2 into LDS (fp16)
+// The loop starts at i = -2 so that the first two iterations only prepare.
+#pragma once
+#include <type_traits>
+
+#include "gdn_device.h"
+#include "gdn_kernels.h"
+#include "gdn_pipe.h"
+
+namespace gdn {
+
+typedef __attribute__((ext_vector_type(8))) _Float16 h8;
+typedef __attribute__((ext_vector_type(4))) _Float16 h4;
+typedef __attribute__((ext_vector_type(2))) _Float16 h2;
+typedef __attribute__((ext_vector_type(2))) float f2;
+
+__device__ __forceinline__ f32x4 mfma_h(h8 a, h8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ h8 cat_h(h4 a, h4 b) {
+    return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+__device__ __forceinline__ h4 to_h4(f32x4 x) { return __builtin_convertvector(x, h4); }
+__device__ __forceinline__ h4 zero_h4() { return h4{0, 0, 0, 0}; }
+
+// Two bf16 (one 32-bit word) to two fp16.
+__device__ __forceinline__ unsigned bf2_to_h2(unsigned w) {
+    const f2 f = {__builtin_bit_cast(float, w << 16), __builtin_bit_cast(float, w & 0xffff0000u)};
+    return __builtin_bit_cast(unsigned, __builtin_convertvector(f, h2));
+}
+
+constexpr int kFastPrep = 4;
+
+template <int C, int DK, int NS, bool ETA>
+struct alignas(16) FastLds {
+    static constexpr int NT = C / 16;                 // 16-token blocks per chunk
+    static constexpr int NB = NT * (NT + 1) / 2;      // blocks on and below the diagonal
+    static constexpr int NOFF = NT * (NT - 1) / 2;    // blocks below the diagonal
+    static constexpr int KP = DK + 8;                 // key / query row stride (fp16)
+    static constexpr int CP = C + 4;                  // transposed-key row stride (fp16)
+    static constexpr int BP = 20;                     // row stride of 16 x 16 blocks
+    static constexpr int bidx(int b, int c) { return b * (b + 1) / 2 + c; }
+    static constexpr int oidx(int b, int c) { return b * (b - 1) / 2 + c; }
+    // keys and queries by chunk parity; each 32-element block of a row in the
+    // scan's k-order (elements 4h..4h+3 then 16+4h..16+4h+3, h = 0..3), so an
+    // MFMA operand slice is one aligned 16-byte read
+    _Float16 K[2][C][KP];
+    _Float16 Q[2][C][KP];
+    _Float16 Kt[2][DK][CP];                    // keys transposed, natural token order
+    _Float16 Tb[2][NB][16][BP];                // T = (I - A)^{-1}, blocks (b, c <= b)
+    _Float16 Pb[2][NB][16][BP];                // masked decayed scores, blocks (b, c <= b)
+    _Float16 Ao[2][NOFF > 0 ? NOFF : 1][16][BP];   // A below the diagonal blocks
+    float Ad[2][NT][16][BP];                   // diagonal blocks of A (fp32, for the solve)
+    // per-token vectors, three chunks live at a time
+    float g2[3][C];    // inclusive cumsum of log2 alpha
+    float er[3][C];    // 2^(g2_r - g2_ref): row factor of exp(g_r - g_i)
+    float fi[3][C];    // 2^(g2_ref - g2_i): column factor
+    float eg[3][C];    // exp(g)
+    float dec[3][C];   // exp(g_last - g)
+    float beta[3][C];
+    float eta[ETA ? 3 : 1][ETA ? C : 4];   // write strength
+    float bge[ETA ? 3 : 1][ETA ? C : 4];   // beta exp(g)
+    float glast[4];    // exp(g_last)
+    int sep[4];        // row x column factors safe in fp32 for this chunk
+};
+
+// Row strips of the Gram / score formation: strip rt holds the tiles
+// (rt, ct) for ct = 0..rt of both A and the scores P, and the transposition
+// of key block rt.  Strips go to prep waves 1..3 so that the tile counts
+// balance: the last strip alone, the one before alone, the rest together.
+template <int NT>
+struct FastStrips {
+    static constexpr int owner(int rt) {
+        const int from_last = NT - 1 - rt;
+        return 1 + (from_last < 2 ? from_last : 2);
+    }
+    static constexpr int count(int w) {
+        int n = 0;
+        for (int rt = 0; rt < NT; ++rt) n += owner(rt) == w;
+        return n;
+    }
+    // j-th strip of wave w, largest first
+    static constexpr int strip(int w, int j) {
+        for (int rt = NT - 1; rt >= 0; --rt)
+            if (owner(rt) == w) {
+                if (j == 0) return rt;
+                --j;
+            }
+        return -1;
+    }
+};
+
+template <int C, int DK, int NS, bool ETA>
+__global__ __launch_bounds__((NS + kFastPrep) * 64) void gdn_fwd_fast_kernel(FwdParams p) {
+    constexpr int NP = kFastPrep;
+    using L = FastLds<C, DK, NS, ETA>;
+    using ST = FastStrips<C / 16>;
+    constexpr int NT = C / 16;
+    constexpr int NK = DK / 16;              // 16-row tiles of S^T
+    constexpr int NSS = DK / 32;             // k-steps over d_k
+    constexpr int NTS = (C + 31) / 32;       // k-steps over the tokens of a chunk
+    constexpr int DVT = 16 * NS;
+    constexpr int KV = C * DK / 8;           // 16-byte vectors in a key tile
+    constexpr int NSTG = NP - 1;
+    constexpr int NKV = (KV + 64 * NSTG - 1) / (64 * NSTG);
+    static_assert(DK % 32 == 0 && C % 16 == 0, "shape");
+    static_assert(sizeof(L) <= 160 * 1024, "LDS budget");
+    __shared__ L s;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int n = lane & 15;
+    const int h = lane >> 4;
+    const bool scan = wave < NS;
+    const int pw = wave - NS;
+    const int plane = tid - (NS + 1) * 64;   // 0..64*NSTG-1 on prep waves 1..NP-1
+
+    int tile, bh;
+    if (p.xcd_groups) {
+        const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+        tile = slot % p.n_tiles;
+        bh = xcd + 8 * (slot / p.n_tiles);
+    } else {
+        tile = blockIdx.x % p.n_tiles;
+        bh = blockIdx.x / p.n_tiles;
+    }
+    const int T = p.T, dv = p.dv;
+    const int nchunks = (T + C - 1) / C;
+    const __bf16* kb = reinterpret_cast<const __bf16*>(p.k) + (size_t)bh * T * DK;
+    const __bf16* qb = reinterpret_cast<const __bf16*>(p.q) + (size_t)bh * T * DK;
+    const __bf16* vb = reinterpret_cast<const __bf16*>(p.v) + (size_t)bh * T * dv;
+    const float* ab = p.alpha ? p.alpha + (size_t)bh * T : nullptr;
+    const float* bb = p.beta + (size_t)bh * T;
+    const float* eb = p.eta ? p.eta + (size_t)bh * T : nullptr;
+    const buf_t kbuf = buffer_over(kb, (uint32_t)T * DK * 2);
+    const buf_t qbuf = buffer_over(qb, (uint32_t)T * DK * 2);
+    const int col0 = tile * DVT + 16 * wave;   // scan waves: first value column
+
+    auto mod3 = [](int x) { return (x + 3) % 3; };   // x >= -3
+
+    if (!scan) {
+        // ============================== prep ===============================
+        // raw bf16 key / query tiles of the next chunk to stage: loaded an
+        // iteration ahead, converted into LDS, then reloaded with the next
+        uint4 stK[NKV], stQ[NKV];
+        float stA = 1.f, stB = 0.f, stE = 0.f;  // prep 0: gates of the next chunk to prepare
+
+        // prep 1+: global loads of chunk cc's keys and queries (rows past the
+        // end of the sequence read as zero)
+        auto kq_load = [&](int cc) __attribute__((always_inline)) {
+            const int t0 = cc * C;
+            static_for<0, NKV>([&](auto I) {
+                constexpr int i = decltype(I)::value;
+                const int vi = plane + i * 64 * NSTG;
+                if (i + 1 < NKV || vi < KV) {
+                    const int r = vi / (DK / 8), c8 = (vi % (DK / 8)) * 8;
+                    stK[i] = buf_load_16B(kbuf, 2u * ((t0 + r) * DK + c8));
+                    stQ[i] = buf_load_16B(qbuf, 2u * ((t0 + r) * DK + c8));
+                }
+            });
+        };
+        // prep 1+: chunk cc's keys and queries into LDS as fp16, in k-order
+        auto kq_store = [&](int cc) __attribute__((always_inline)) {
+            const int buf = cc & 1;
+            static_for<0, NKV>([&](auto I) {
+                constexpr int i = decltype(I)::value;
+                const int vi = plane + i * 64 * NSTG;
+                if (i + 1 < NKV || vi < KV) {
+                    const int r = vi / (DK / 8), c8 = (vi % (DK / 8)) * 8;
+                    const uint4 kv = stK[i], qv = stQ[i];
+                    *reinterpret_cast<uint2*>(&s.K[buf][r][kq_pos(c8)]) =
+                        make_uint2(bf2_to_h2(kv.x), bf2_to_h2(kv.y));
+                    *reinterpret_cast<uint2*>(&s.K[buf][r][kq_pos(c8 + 4)]) =
+                        make_uint2(bf2_to_h2(kv.z), bf2_to_h2(kv.w));
+                    *reinterpret_cast<uint2*>(&s.Q[buf][r][kq_pos(c8)]) =
+                        make_uint2(bf2_to_h2(qv.x), bf2_to_h2(qv.y));
+                    *reinterpret_cast<uint2*>(&s.Q[buf][r][kq_pos(c8 + 4)]) =
+                        make_uint2(bf2_to_h2(qv.z), bf2_to_h2(qv.w));
+                }
+            });
+        };
+        // prep 0: gates of chunk cc (lane t holds token t of the chunk)
+        auto gate_load = [&](int cc) __attribute__((always_inline)) {
+            const int t0 = cc * C, Lc = min(C, T - t0);
+            const int tt = t0 + min(lane, Lc - 1);
+            stA = ab ? ab[tt] : 1.f;
+            stB = bb[tt];
+            if constexpr (ETA) stE = eb[tt];
+        };
+        // prep 0: decay vectors of chunk cc into vector buffer mod3(cc);
+        // padding tokens are identity transitions (alpha = 1, beta = eta = 0)
+        auto vectors = [&](int cc) __attribute__((always_inline)) {
+            const int vb3 = mod3(cc);
+            const int Lc = min(C, T - cc * C);
+            const float a = lane < Lc ? stA : 1.f;
+            const float l2 = (lane < C) ? __builtin_amdgcn_logf(a) : 0.f;
+            const float g = wave_inclusive_scan(l2, lane);
+            const float gl = lane_value(g, C - 1);
+            // exp(g_r - g_i) = 2^(g2_r - ref) 2^(ref - g2_i), ref the middle of
+            // the chunk, when the chunk's decay range keeps both factors far
+            // inside fp32; otherwise each ratio is exponentiated on its own
+            const float ref = lane_value(g, C / 2);
+            const float g0 = lane_value(g, 0);
+            if (lane < C) {
+                const float bt = lane < Lc ? stB : 0.f;
+                s.g2[vb3][lane] = g;
+                s.eg[vb3][lane] = __builtin_amdgcn_exp2f(g);
+                s.dec[vb3][lane] = __builtin_amdgcn_exp2f(gl - g);
+                s.beta[vb3][lane] = bt;
+                if constexpr (ETA) {
+                    s.eta[vb3][lane] = lane < Lc ? stE : 0.f;
+                    s.bge[vb3][lane] = bt * __builtin_amdgcn_exp2f(g);
+                }
+                s.er[vb3][lane] = __builtin_amdgcn_exp2f(g - ref);
+                s.fi[vb3][lane] = __builtin_amdgcn_exp2f(ref - g);
+            }
+            if (lane == 0) {
+                s.glast[vb3] = __builtin_amdgcn_exp2f(gl);
+                s.sep[vb3] = (g0 - gl) <= 96.f;
+            }
+        };
+        // prep 1+: the row strips of chunk cc owned by this wave.  Strip rt:
+        // key block rt (B operand of A's tiles), query block rt (B operand
+        // of the scores) and each key block ct <= rt (A operand of both) are
+        // read from LDS once; then the tiles are formed,
+        //   A_ri = -beta_r exp(g_r - g_i) k_r.k_i (i < r),  P_ri = exp(g_r - g_i) q_r.k_i (i <= r),
+        // with lane (n, h) holding row r = 16 rt + n, columns 16 ct + 4 h + e.
+        // The same key block is transposed into Kt by MFMAs against 0/1
+        // selectors: with A the key rows of a 16 x 32 slice and B selecting
+        // slice element 16 u + n', lane (n', h) receives tokens 4h..4h+3 at
+        // dimension 16 u + n' -- four consecutive tokens of one row of K^T
+        // (exact: one product with 1 per output).
+        auto strips = [&](auto W, int cc) __attribute__((always_inline)) {
+            constexpr int w = decltype(W)::value;
+            const int buf = cc & 1;
+            const int vb3 = mod3(cc);
+            // element e of lane (n, h) in the k-order stands for slice position
+            // pos(e) = e < 4 ? 4h + e : 16 + 4h + e - 4
+            h8 sel0, sel1;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int pos = e < 4 ? 4 * h + e : 16 + 4 * h + (e - 4);
+                sel0[e] = (_Float16)(pos == n ? 1.f : 0.f);
+                sel1[e] = (_Float16)(pos == 16 + n ? 1.f : 0.f);
+            }
+            const bool sep = s.sep[vb3];
+            static_for<0, ST::count(w)>([&](auto JJ) {
+                constexpr int rt = ST::strip(w, decltype(JJ)::value);
+                const int r = 16 * rt + n;
+                h8 kb[NSS], qb[NSS];
+#pragma unroll
+                for (int ss = 0; ss < NSS; ++ss) {
+                    kb[ss] = *reinterpret_cast<const h8*>(&s.K[buf][r][32 * ss + 8 * h]);
+                    qb[ss] = *reinterpret_cast<const h8*>(&s.Q[buf][r][32 * ss + 8 * h]);
+                }
+                const float nbr = -s.beta[vb3][r];
+                const float g2r = s.g2[vb3][r];
+                const float err = s.er[vb3][r];
+                static_for<0, rt + 1>([&](auto CC) {
+                    constexpr int ct = decltype(CC)::value;
+                    h8 ka[NSS];
+#pragma unroll
+                    for (int ss = 0; ss < NSS; ++ss) {
+                        if constexpr (ct == rt) ka[ss] = kb[ss];
+                        else ka[ss] = *reinterpret_cast<const h8*>(&s.K[buf][16 * ct + n][32 * ss + 8 * h]);
+                    }
+                    f32x4 ga = zero4(), gp = zero4();
+#pragma unroll
+                    for (int ss = 0; ss < NSS; ++ss) {
+                        ga = mfma_h(ka[ss], kb[ss], ga);
+                        gp = mfma_h(ka[ss], qb[ss], gp);
+                    }
+                    const int i0 = 16 * ct + 4 * h;
+                    f32x4 d;
+                    if (sep) {
+                        d = err * *reinterpret_cast<const f32x4*>(&s.fi[vb3][i0]);
+                    } else {
+                        const f32x4 g2i = *reinterpret_cast<const f32x4*>(&s.g2[vb3][i0]);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) d[e] = __builtin_amdgcn_exp2f(g2r - g2i[e]);
+                    }
+                    f32x4 va, vp;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        va[e] = (ct < rt || i0 + e < r) ? nbr * d[e] * ga[e] : 0.f;
+                        vp[e] = (ct < rt || i0 + e <= r) ? d[e] * gp[e] : 0.f;
+                    }
+                    *reinterpret_cast<h4*>(&s.Pb[buf][L::bidx(rt, ct)][n][4 * h]) = to_h4(vp);
+                    if constexpr (ct == rt)
+                        *reinterpret_cast<f32x4*>(&s.Ad[buf][rt][n][4 * h]) = va;
+                    else
+                        *reinterpret_cast<h4*>(&s.Ao[buf][L::oidx(rt, ct)][n][4 * h]) = to_h4(va);
+                });
+                // key block rt transposed
+#pragma unroll
+                for (int ss = 0; ss < NSS; ++ss) {
+                    const f32x4 d0 = mfma_h(kb[ss], sel0, zero4());
+                    const f32x4 d1 = mfma_h(kb[ss], sel1, zero4());
+                    *reinterpret_cast<h4*>(&s.Kt[buf][32 * ss + n][16 * rt + 4 * h]) = to_h4(d0);
+                    *reinterpret_cast<h4*>(&s.Kt[buf][32 * ss + 16 + n][16 * rt + 4 * h]) = to_h4(d1);
+                }
+            });
+        };
+        // prep 0: T_bb = (I - A_bb)^{-1} for all diagonal blocks of chunk cc:
+        // lane (b, i) computes row i of T_bb from T = I + T A by substitution
+        // from the last column down,  T[i][k] = [i == k] + sum_{m > k} T[i][m] A[m][k],
+        // adding each final T[i][m] into every earlier column's partial sum.
+        auto diag_solve = [&](int cc) __attribute__((always_inline)) {
+            const int buf = cc & 1;
+            if (lane < 16 * NT) {
+                const int b = lane >> 4, i = lane & 15;
+                float part[16];
+#pragma unroll
+                for (int k = 0; k < 16; ++k) part[k] = (k == i) ? 1.f : 0.f;
+                float x[16];
+                f32x4 abuf[3][4];
+                auto load_row = [&](auto M) __attribute__((always_inline)) {
+                    constexpr int m = decltype(M)::value;
+#pragma unroll
+                    for (int q = 0; 4 * q < m; ++q)
+                        abuf[m % 3][q] = *reinterpret_cast<const f32x4*>(&s.Ad[buf][b][m][4 * q]);
+                };
+                load_row(std::integral_constant<int, 15>{});
+                load_row(std::integral_constant<int, 14>{});
+                static_for<0, 16>([&](auto JJ) {
+                    constexpr int m = 15 - decltype(JJ)::value;
+                    if constexpr (m - 2 > 0) load_row(std::integral_constant<int, m - 2>{});
+                    x[m] = part[m];
+#pragma unroll
+                    for (int q = 0; 4 * q < m; ++q) {
+                        const f32x4 a = abuf[m % 3][q];
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            if (4 * q + e < m) part[4 * q + e] = fmaf(x[m], a[e], part[4 * q + e]);
+                    }
+                });
+                _Float16* trow = &s.Tb[buf][L::bidx(b, b)][i][0];
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    *reinterpret_cast<h4*>(trow + 4 * q) =
+                        to_h4(f32x4{x[4 * q], x[4 * q + 1], x[4 * q + 2], x[4 * q + 3]});
+            }
+        };
+        // prep 0: the blocks of T below the diagonal of chunk cc, by distance
+        // from the diagonal:  T_bc = T_bb R,  R = sum_{c<=k<b} A_bk T_kc.
+        // Lane (n, h) holds T_bc[4h + j][n] (accumulator layout), which is
+        // also the B-operand layout of the next products.
+        auto t_off = [&](int cc) __attribute__((always_inline)) {
+            if constexpr (NT > 1) {
+                const int buf = cc & 1;
+                h4 Tr[NT][NT];
+                // column n, rows 4h..4h+3 of a diagonal block of T
+                auto diag_col = [&](int c) __attribute__((always_inline)) {
+                    h4 v;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) v[j] = s.Tb[buf][L::bidx(c, c)][4 * h + j][n];
+                    return v;
+                };
+                h4 Tdiag[NT];
+                static_for<0, NT - 1>([&](auto CC) {
+                    constexpr int c = decltype(CC)::value;
+                    Tdiag[c] = diag_col(c);
+                });
+                static_for<1, NT>([&](auto DD) {
+                    constexpr int d = decltype(DD)::value;
+                    static_for<0, NT - d>([&](auto CC) {
+                        constexpr int c = decltype(CC)::value;
+                        constexpr int b = c + d;
+                        f32x4 R = zero4();
+                        static_for<0, (d + 1) / 2>([&](auto KK) {
+                            constexpr int k = c + 2 * decltype(KK)::value;
+                            const h4 a0 = *reinterpret_cast<const h4*>(&s.Ao[buf][L::oidx(b, k)][n][4 * h]);
+                            h4 t0;
+                            if constexpr (k == c) t0 = Tdiag[c];
+                            else t0 = Tr[k][c];
+                            h4 a1 = zero_h4(), t1 = zero_h4();
+                            if constexpr (k + 1 < b) {
+                                a1 = *reinterpret_cast<const h4*>(&s.Ao[buf][L::oidx(b, k + 1)][n][4 * h]);
+                                t1 = Tr[k + 1][c];
+                            }
+                            R = mfma_h(cat_h(a0, a1), cat_h(t0, t1), R);
+                        });
+                        const h4 tbb = *reinterpret_cast<const h4*>(&s.Tb[buf][L::bidx(b, b)][n][4 * h]);
+                        const f32x4 tbc = mfma_h(cat_h(tbb, zero_h4()), cat_h(to_h4(R), zero_h4()), zero4());
+                        Tr[b][c] = to_h4(tbc);
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) s.Tb[buf][L::bidx(b, c)][4 * h + j][n] = Tr[b][c][j];
+                    });
+                });
+            }
+        };
+        // stage-parity output: T of chunk cc as fp32 [C][C] (upper part zero)
+        auto dbg_t = [&](int cc) __attribute__((always_inline)) {
+            {
+                {
+                    const int buf = cc & 1;
+                    float* dst = p.dbg_T + ((size_t)bh * nchunks + cc) * C * C;
+                    for (int e = lane; e < C * C; e += 64) {
+                        const int r = e / C, c = e % C;
+                        const int b = r / 16, cb = c / 16;
+                        dst[e] = cb <= b ? (float)s.Tb[buf][L::bidx(b, cb)][r % 16][c % 16] : 0.f;
+                    }
+                }
+            }
+        };
+
+        auto prep_role = [&](auto W) __attribute__((always_inline)) {
+            constexpr int w = decltype(W)::value;
+            auto step = [&](auto PAR, int i) __attribute__((always_inline)) {
+                constexpr int par = decltype(PAR)::value;   // parity of i
+                // ---- phase A ----
+                if constexpr (w == 0) {
+                    if (i >= 0) {
+                        t_off(i);
+                        if (p.dbg_T) {
+                            wave_lds_sync();
+                            dbg_t(i);
+                        }
+                    }
+                } else {
+                    if (i + 1 >= 0 && i + 1 < nchunks) strips(W, i + 1);
+                }
+                __syncthreads();
+                // ---- phase B ----
+                if constexpr (w == 0) {
+                    if (i + 2 < nchunks) {
+                        vectors(i + 2);
+                        if (i + 3 < nchunks) gate_load(i + 3);
+                    }
+                    if (i + 1 >= 0 && i + 1 < nchunks) diag_solve(i + 1);
+                } else {
+                    if (i + 2 < nchunks) {
+                        kq_store(i + 2);
+                        if (i + 3 < nchunks) kq_load(i + 3);
+                    }
+                }
+                __syncthreads();
+            };
+            if constexpr (w == 0) gate_load(0);
+            else kq_load(0);
+            for (int i = -2; i < nchunks; i += 2) {
+                step(std::integral_constant<int, 0>{}, i);
+                if (i + 1 < nchunks) step(std::integral_constant<int, 1>{}, i + 1);
+            }
+        };
+        switch (pw) {
+            case 0: prep_role(std::integral_constant<int, 0>{}); break;
+            case 1: prep_role(std::integral_constant<int, 1>{}); break;
+            case 2: prep_role(std::integral_constant<int, 2>{}); break;
+            default: prep_role(std::integral_constant<int, 3>{}); break;
+        }
+    } else {
+        // ============================== scan ===============================
+        f32x4 Sacc[NK];            // Sacc[t][j] = S[col0 + n][16 t + 4 h + j]
+        // value rows of the next chunk, A operand of the transposing MFMA:
+        // lane (n, h) holds V[16 rt + n][col0 + 8 (h & 1) .. + 7] (lanes h >= 2
+        // repeat lanes h - 2; the selector gives them weight zero)
+        uint4 vraw[NT];
+        const buf_t vbuf = buffer_over(vb, (uint32_t)T * dv * 2);
+        const uint32_t voff = 2u * (n * dv + col0 + 8 * (h & 1));
+        auto v_load = [&](int cc) __attribute__((always_inline)) {
+            const uint32_t t0 = (uint32_t)cc * C;
+#pragma unroll
+            for (int rt = 0; rt < NT; ++rt) vraw[rt] = buf_load_16B(vbuf, voff + 2u * (t0 + 16 * rt) * dv);
+        };
+        // selector picking value column n of the 16 (lane (n, h), k-slots 8h..8h+7)
+        bf16x8 vsel;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) vsel[e] = (__bf16)((h < 2 && 8 * h + e == n) ? 1.f : 0.f);
+
+        const int osz = p.o_bf16 ? 2 : 4;
+        const buf_t obuf = buffer_over(reinterpret_cast<const char*>(p.O) + (size_t)bh * T * dv * osz,
+                                       (uint32_t)T * dv * osz);
+        const size_t sb = (size_t)bh * dv * DK + (size_t)(col0 + n) * DK;
+#pragma unroll
+        for (int t = 0; t < NK; ++t)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) Sacc[t][j] = p.S0 ? p.S0[sb + 16 * t + 4 * h + j] : 0.f;
+        v_load(0);
+        // wait here for the initial state (and the first values): at the loop
+        // head the state registers must not look like pending loads, or every
+        // iteration would wait for all outstanding memory operations,
+        // including the previous chunk's output stores
+        __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0)
+        // the two preparation-only iterations
+        for (int i = 0; i < 4; ++i) __syncthreads();
+
+        // token-pair operands of the k-steps over the chunk (tiles 2s, 2s+1)
+        auto pair_op = [&](const f32x4* tiles, int sidx) __attribute__((always_inline)) {
+            return cat_h(to_h4(tiles[2 * sidx]), 2 * sidx + 1 < NT ? to_h4(tiles[2 * sidx + 1]) : zero_h4());
+        };
+        // one chunk; PAR = parity of c (the LDS buffer of K, Q, Kt, T and P)
+        auto chunk = [&](auto PAR, int c) __attribute__((always_inline)) {
+            constexpr int buf = decltype(PAR)::value;
+            const int vb3 = c % 3;
+            const int t0 = c * C;
+            // ---- phase A: X = K S^T, Z^T = S Q^T ----
+            h8 sh[NSS];
+#pragma unroll
+            for (int ss = 0; ss < NSS; ++ss) sh[ss] = cat_h(to_h4(Sacc[2 * ss]), to_h4(Sacc[2 * ss + 1]));
+            f32x4 X[NT], Zt[NT];
+#pragma unroll
+            for (int rt = 0; rt < NT; ++rt) { X[rt] = zero4(); Zt[rt] = zero4(); }
+#pragma unroll
+            for (int ss = 0; ss < NSS; ++ss) {
+                h8 kf[NT], qf[NT];
+#pragma unroll
+                for (int rt = 0; rt < NT; ++rt) {
+                    kf[rt] = *reinterpret_cast<const h8*>(&s.K[buf][16 * rt + n][32 * ss + 8 * h]);
+                    qf[rt] = *reinterpret_cast<const h8*>(&s.Q[buf][16 * rt + n][32 * ss + 8 * h]);
+                }
+#pragma unroll
+                for (int rt = 0; rt < NT; ++rt) X[rt] = mfma_h(kf[rt], sh[ss], X[rt]);
+#pragma unroll
+                for (int rt = 0; rt < NT; ++rt) Zt[rt] = mfma_h(sh[ss], qf[rt], Zt[rt]);
+            }
+            // per-token vectors of chunk c for phase B (in LDS since an
+            // iteration ago): read now, so that their latency hides behind the
+            // products above
+            const float* f1b = ETA ? &s.eta[vb3][0] : &s.beta[vb3][0];
+            const float* f2b = ETA ? &s.bge[vb3][0] : &s.eg[vb3][0];
+            f32x4 f1[NT], f2[NT], fd[NT];
+            float egr[NT];
+#pragma unroll
+            for (int rt = 0; rt < NT; ++rt) {
+                f1[rt] = *reinterpret_cast<const f32x4*>(f1b + 16 * rt + 4 * h);
+                f2[rt] = *reinterpret_cast<const f32x4*>(f2b + 16 * rt + 4 * h);
+                fd[rt] = *reinterpret_cast<const f32x4*>(&s.dec[vb3][16 * rt + 4 * h]);
+                egr[rt] = s.eg[vb3][16 * rt + n];
+            }
+            const float gl = s.glast[vb3];
+            __syncthreads();
+            // ---- phase B ----
+            // T of this chunk (its blocks below the diagonal were formed in phase A)
+            h8 top[NT][NTS];
+            static_for<0, NT>([&](auto BB) {
+                constexpr int b = decltype(BB)::value;
+                static_for<0, b / 2 + 1>([&](auto SS) {
+                    constexpr int sidx = decltype(SS)::value;
+                    const h4 t0_ = *reinterpret_cast<const h4*>(&s.Tb[buf][L::bidx(b, 2 * sidx)][n][4 * h]);
+                    h4 t1_ = zero_h4();
+                    if constexpr (2 * sidx + 1 <= b)
+                        t1_ = *reinterpret_cast<const h4*>(&s.Tb[buf][L::bidx(b, 2 * sidx + 1)][n][4 * h]);
+                    top[b][sidx] = cat_h(t0_, t1_);
+                });
+            });
+            // this chunk's values in the accumulator layout (token 16 rt + 4 h + j, column n)
+            f32x4 Vt[NT];
+#pragma unroll
+            for (int rt = 0; rt < NT; ++rt)
+                Vt[rt] = mfma_bf16(__builtin_bit_cast(bf16x8, vraw[rt]), vsel, zero4());
+            if (c + 1 < nchunks) v_load(c + 1);
+            // right-hand side Y = diag(beta) (V - diag(exp g) X)  (or eta V - beta exp(g) X)
+            f32x4 Y[NT];
+#pragma unroll
+            for (int rt = 0; rt < NT; ++rt)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    Y[rt][j] = ETA ? f1[rt][j] * Vt[rt][j] - f2[rt][j] * X[rt][j]
+                                   : f1[rt][j] * (Vt[rt][j] - f2[rt][j] * X[rt][j]);
+            h8 yh[NTS];
+#pragma unroll
+            for (int ss = 0; ss < NTS; ++ss) yh[ss] = pair_op(Y, ss);
+            // V' = T Y (T lower block triangular: row block b uses k-steps s <= b / 2)
+            f32x4 Vp[NT];
+            static_for<0, NT>([&](auto BB) {
+                constexpr int b = decltype(BB)::value;
+                f32x4 acc = zero4();
+                static_for<0, b / 2 + 1>([&](auto SS) {
+                    constexpr int sidx = decltype(SS)::value;
+                    acc = mfma_h(top[b][sidx], yh[sidx], acc);
+                });
+                Vp[b] = acc;
+            });
+            if (p.dbg_V) {
+                // stage output: V' rows of this chunk (rows past the end of the
+                // sequence fall outside the buffer and are dropped)
+                const buf_t dbuf = buffer_over(p.dbg_V + (size_t)bh * T * dv, (uint32_t)T * dv * 4);
+                const uint32_t lane_off = 4u * ((uint32_t)(t0 + 4 * h) * dv + col0 + n);
+#pragma unroll
+                for (int rt = 0; rt < NT; ++rt)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        // (a bit_cast of the vector component itself stored
+                        // component 0 four times; copy it out first)
+                        const float e = Vp[rt][j];
+                        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(e), dbuf, (int)lane_off,
+                                                              (int)(4u * (16 * rt + j) * dv), 0);
+                    }
+            }
+            h8 vh[NTS];
+#pragma unroll
+            for (int ss = 0; ss < NTS; ++ss) vh[ss] = pair_op(Vp, ss);
+            // S^T <- exp(g_last) S^T + K^T diag(exp(g_last - g)) V'
+            f32x4 Vd[NT];
+#pragma unroll
+            for (int rt = 0; rt < NT; ++rt) Vd[rt] = fd[rt] * Vp[rt];
+            h8 vd[NTS];
+#pragma unroll
+            for (int ss = 0; ss < NTS; ++ss) vd[ss] = pair_op(Vd, ss);
+#pragma unroll
+            for (int t = 0; t < NK; ++t) Sacc[t] *= gl;
+#pragma unroll
+            for (int ss = 0; ss < NTS; ++ss) {
+                h8 kt[NK];
+#pragma unroll
+                for (int t = 0; t < NK; ++t) {
+                    const _Float16* row = &s.Kt[buf][16 * t + n][0];
+                    const h4 a = *reinterpret_cast<const h4*>(row + 32 * ss + 4 * h);
+                    const h4 b = 32 * ss + 16 < C ? *reinterpret_cast<const h4*>(row + 32 * ss + 16 + 4 * h)
+                                                  : zero_h4();
+                    kt[t] = cat_h(a, b);
+                }
+#pragma unroll
+                for (int t = 0; t < NK; ++t) Sacc[t] = mfma_h(kt[t], vd[ss], Sacc[t]);
+            }
+            // O^T = diag(exp g) Z^T + V'^T P^T  (lane: row 16 rt + n, columns 4h..4h+3);
+            // output rows past the end of the sequence fall outside the buffer (dropped)
+            static_for<0, NT>([&](auto RR) {
+                constexpr int rt = decltype(RR)::value;
+                f32x4 acc = zero4();
+                static_for<0, rt / 2 + 1>([&](auto SS) {
+                    constexpr int sidx = decltype(SS)::value;
+                    const h4 p0 = *reinterpret_cast<const h4*>(&s.Pb[buf][L::bidx(rt, 2 * sidx)][n][4 * h]);
+                    h4 p1 = zero_h4();
+                    if constexpr (2 * sidx + 1 <= rt)
+                        p1 = *reinterpret_cast<const h4*>(&s.Pb[buf][L::bidx(rt, 2 * sidx + 1)][n][4 * h]);
+                    acc = mfma_h(vh[sidx], cat_h(p0, p1), acc);
+                });
+                const f32x4 o = egr[rt] * Zt[rt] + acc;
+                const uint32_t row = (uint32_t)(t0 + 16 * rt + n) * dv + col0 + 4 * h;
+                if (p.o_bf16) buf_store(obuf, row * 2, __builtin_convertvector(o, bf16x4));
+                else buf_store(obuf, row * 4, o);
+            });
+            __syncthreads();
+        };
+        for (int c = 0; c < nchunks; c += 2) {
+            chunk(std::integral_constant<int, 0>{}, c);
+            if (c + 1 < nchunks) chunk(std::integral_constant<int, 1>{}, c + 1);
+        }
+#pragma unroll
+        for (int t = 0; t < NK; ++t)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) p.S_final[sb + 16 * t + 4 * h + j] = Sacc[t][j];
+    }
+}
+
+}  // namespace gdn

@@ -1,0 +1,30 @@
+// gdn_inst_fast.hip -- instantiations of the fp16-operand fused kernel for
+// one (chunk, d_k) pair, given on the command line as GDN_C and GDN_DK.
+#include "gdn_fast.h"
+#include "gdn_launch.h"
+
+#if !defined(GDN_C) || !defined(GDN_DK)
+#error "build with -DGDN_C=<chunk> -DGDN_DK=<d_k>"
+#endif
+
+#define GDN_NAME2(CC, KK) fast_launcher_c##CC##_d##KK
+#define GDN_NAME(CC, KK) GDN_NAME2(CC, KK)
+
+namespace gdn {
+namespace {
+template <int NS, bool ETA>
+void launch(const FwdParams& p, long nblocks, hipStream_t st) {
+    hipLaunchKernelGGL((gdn_fwd_fast_kernel<GDN_C, GDN_DK, NS, ETA>), dim3((unsigned)nblocks),
+                       dim3((NS + kFastPrep) * 64), 0, st, p);
+}
+}  // namespace
+
+FwdLauncher GDN_NAME(GDN_C, GDN_DK)(int ns, bool eta) {
+    switch (ns) {
+        case 1: return eta ? launch<1, true> : launch<1, false>;
+        case 2: return eta ? launch<2, true> : launch<2, false>;
+        case 4: return eta ? launch<4, true> : launch<4, false>;
+    }
+    return nullptr;
+}
+}  // namespace gdn

@@ -44,6 +44,8 @@ struct FwdParams {
     int o_bf16;           // O stored as bf16 (else fp32)
     int xcd_groups;       // pipelined kernel: place a head's tiles on one XCD
     const float* eta;     // write strength; may be null: eta = beta
+    float* dbg_T;         // fast kernel, stage output: T per chunk [B,H,NT,C,C] (may be null)
+    float* dbg_V;         // fast kernel, stage output: pseudo-values V' [B,H,T,d_v] (may be null)
 };
 
 // LDS layout of one workgroup.  Rows are padded by 16 bytes.

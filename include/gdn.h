@@ -62,12 +62,22 @@ typedef struct {
 /*
  * Supported combinations (anything else that is well-formed returns
  * GDN_ERR_UNSUPPORTED):
- *   qkv_dtype GDN_BF16: chunk_size in {32, 64}, d_k in {32, 64, 128},
- *                       d_v a multiple of 16 in [16, 1024];
- *   qkv_dtype GDN_F32:  chunk_size in {16, 32, 64}, d_k in {16, 32, 64},
- *                       d_v a multiple of 16 in [16, 1024].
+ *   qkv_dtype GDN_BF16: chunk_size in {16, 32, 64} and d_k in {32, 64, 96,
+ *                       128}, or d_k = 256 with chunk_size in {16, 32};
+ *   qkv_dtype GDN_F32:  chunk_size in {16, 32, 64}, d_k in {16, 32, 64};
+ *   d_v a multiple of 16 in [16, 1024]; one head's largest tensor (T x
+ *   max(d_k, d_v) x 4 bytes) below 2 GiB.
  * T may be any value >= 1; a last chunk shorter than chunk_size is handled
  * exactly (padding tokens are identity transitions).
+ *
+ * Arithmetic.  bf16 inputs run one fused kernel whose matrix products take
+ * fp16 operands (11 significant bits; bf16 inputs convert exactly) with fp32
+ * accumulation and an fp32 state: against the exact result the normwise
+ * error is near 6e-4 on gated workloads.  Operands must stay inside the fp16
+ * range (|x| < 65504; the state and the values are the ones that grow).
+ * Without decay and with beta near 2 (reflections) the state keeps every
+ * rounding, so the error grows with the number of chunks; gdn_chunk_fwd_precise
+ * then keeps it near 1e-5.  f32 inputs use fp32 matrix products throughout.
  */
 
 /*
@@ -116,6 +126,43 @@ gdn_status gdn_chunk_fwd_eta(const gdn_shape* s,
                              void* stream);
 
 /*
+ * The same pass with bf16 inputs through the split-bf16 kernels: every
+ * derived matrix-product operand is a pair of bf16 numbers (hi + lo, about
+ * 16 significant bits), which keeps the normwise error near 1e-5 whatever
+ * the gates, at roughly twice the run time of gdn_chunk_fwd.  Shapes: bf16
+ * with chunk_size in {32, 64} and d_k in {64, 128} take the pipelined
+ * split kernel, other supported bf16 and all f32 shapes the generic one
+ * (bf16 chunk_size 16 and d_k 96 / 256 return GDN_ERR_UNSUPPORTED).  eta may
+ * be NULL (eta = beta).  Arguments and conventions as gdn_chunk_fwd_eta,
+ * without a workspace.
+ */
+gdn_status gdn_chunk_fwd_precise(const gdn_shape* s,
+                                 const void* q, const void* k, const void* v,
+                                 const float* alpha, const float* beta, const float* eta,
+                                 const float* S0, void* O, float* S_final,
+                                 void* stream);
+
+/*
+ * gdn_chunk_fwd_eta (bf16 inputs only) with two intermediates of the kernel
+ * written out, for stage-by-stage checks of the pass itself:
+ *   T_out  [B, H, NT, C, C] float: T = (I - A)^{-1} of every chunk as the
+ *          kernel holds it (fp16 values, NT = ceil(T / C); zero above the
+ *          diagonal and, in a ragged last chunk, identity past its end);
+ *          A strictly lower with A_ri = -beta_r exp(g_r - g_i) k_r.k_i
+ *          ("从零开始的 GDN 推导", UT transform, with L = -A);
+ *   Vp_out [B, H, T, d_v] float: the pseudo-values V' = U - W S^T of every
+ *          chunk ("从零开始的 GDN 推导", S update), before their rounding to
+ *          the fp16 operands of the output and state products.
+ * Either may be NULL.  O and S_final are written as by gdn_chunk_fwd_eta.
+ */
+gdn_status gdn_chunk_fwd_stages(const gdn_shape* s,
+                                const void* q, const void* k, const void* v,
+                                const float* alpha, const float* beta, const float* eta,
+                                const float* S0, void* O, float* S_final,
+                                float* T_out, float* Vp_out,
+                                void* stream);
+
+/*
  * Chunk-local quantities of the same method, for inspection and testing of
  * the intermediate stages.  For every chunk c (NT = ceil(T / C) chunks, the
  * last one zero-padded to C tokens):
@@ -126,7 +173,9 @@ gdn_status gdn_chunk_fwd_eta(const gdn_shape* s,
  *   W_out  [B, H, T, d_k] float: W = T diag(beta) diag(exp(g)) K;
  *   U_out  [B, H, T, d_v] float: U = T diag(beta) V ("S 的推导").
  * Any of the three output pointers may be NULL (that output is skipped).
- * Same support matrix and conventions as gdn_chunk_fwd.
+ * Computed by the generic stage kernel (fp32 solve, split-bf16 products):
+ * bf16 with chunk_size in {32, 64} and d_k in {32, 64, 128}, f32 as for
+ * gdn_chunk_fwd; other shapes return GDN_ERR_UNSUPPORTED.
  */
 gdn_status gdn_chunk_prep(const gdn_shape* s,
                           const void* k, const void* v,

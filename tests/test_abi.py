@@ -62,8 +62,9 @@ def fwd(lib, s, **ptrs):
 @pytest.mark.parametrize("kw,expected", [
     (dict(B=0), 2), (dict(H=-1), 2), (dict(T=0), 2), (dict(d_k=0), 2),
     (dict(qkv_dtype=7), 3), (dict(o_dtype=-1), 3),
-    (dict(chunk_size=48), 4), (dict(chunk_size=16), 4), (dict(d_k=256), 4),
+    (dict(chunk_size=48), 4), (dict(d_k=256), 4), (dict(d_k=16), 4), (dict(d_k=48), 4),
     (dict(d_v=40), 4), (dict(d_v=2048), 4), (dict(qkv_dtype=1, d_k=128), 4),
+    (dict(T=5_000_000), 4),
 ])
 def test_bad_shapes_rejected(lib, kw, expected):
     # a mismatched q pointer (odd address) could never reach a launch either
@@ -95,13 +96,34 @@ def test_prep_validation(lib):
                               None, 0, None) == 0
 
 
+def test_new_entries_validate(lib):
+    """gdn_chunk_fwd_precise and gdn_chunk_fwd_stages reject before any launch."""
+    sp = ctypes.byref(shape())
+    odd = ctypes.c_void_p(0x10001)
+    assert lib.gdn_chunk_fwd_precise(None, FAKE, FAKE, FAKE, None, FAKE, None, None, FAKE, FAKE,
+                                     None) == 1
+    assert lib.gdn_chunk_fwd_precise(sp, odd, FAKE, FAKE, None, FAKE, None, None, FAKE, FAKE,
+                                     None) == 4
+    # bf16 chunk 16 has no split-bf16 kernel
+    s16 = ctypes.byref(shape(chunk_size=16))
+    assert lib.gdn_chunk_fwd_precise(s16, FAKE, FAKE, FAKE, None, FAKE, None, None, FAKE, FAKE,
+                                     None) == 4
+    assert lib.gdn_chunk_fwd_stages(sp, None, FAKE, FAKE, None, FAKE, None, None, FAKE, FAKE,
+                                    None, None, None) == 1
+    assert lib.gdn_chunk_fwd_stages(sp, FAKE, FAKE, FAKE, None, FAKE, None, None, FAKE, FAKE,
+                                    ctypes.c_void_p(0x10004), None, None) == 4
+    f32 = ctypes.byref(shape(qkv_dtype=1, d_k=64))
+    assert lib.gdn_chunk_fwd_stages(f32, FAKE, FAKE, FAKE, None, FAKE, None, None, FAKE, FAKE,
+                                    None, None, None) == 4
+
+
 def test_workspace_query_and_strings(lib):
     for kw in (dict(), dict(qkv_dtype=1, d_k=16, d_v=16, chunk_size=16),
-               dict(chunk_size=32), dict(d_v=256)):
+               dict(chunk_size=32), dict(d_v=256), dict(chunk_size=16), dict(d_k=96, d_v=192)):
         assert lib.gdn_chunk_fwd_workspace_bytes(ctypes.byref(shape(**kw))) == 0
     for code in range(7):
         assert lib.gdn_status_string(code).decode()
-    assert lib.gdn_version() >= 100
+    assert lib.gdn_version() >= 200
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
@@ -132,7 +154,9 @@ def rec(lib, s, **ptrs):
     (dict(d_k=48), 4), (dict(d_k=512), 4), (dict(d_v=70000), 4),
 ])
 def test_recurrent_bad_shapes_rejected(lib, kw, expected):
-    assert rec(lib, shape(**kw)) == expected
+    # an odd q pointer as well: even a shape check that wrongly passed could
+    # not reach a launch
+    assert rec(lib, shape(**kw), q=ctypes.c_void_p(0x10001)) == expected
     assert lib.gdn_last_error().decode() != ""
 
 

@@ -114,9 +114,12 @@ def test_null_eta_is_the_plain_entry():
     torch.cuda.synchronize()
     assert torch.equal(O0, O1) and torch.equal(S0, S1)
     # eta given explicitly takes the unfactored right-hand side
-    # diag(eta) V - diag(beta exp g) K S^T: same values up to rounding
-    assert rel_err(O2.cpu().numpy(), O0.cpu().numpy()) < 1e-4
-    assert rel_err(S2.cpu().numpy(), S0.cpu().numpy()) < 1e-4
+    # diag(eta) V - diag(beta exp g) K S^T: the same values up to rounding,
+    # so both lie within the tolerance of the exact result
+    Or, Sr = oracle_eta(x, None)
+    for O_, S_ in ((O0, S0), (O2, S2)):
+        assert rel_err(O_.cpu().numpy(), Or) < TOL["bf16"]
+        assert rel_err(S_.cpu().numpy(), Sr) < TOL["bf16"]
 
 
 def test_random_eta_two_scan_waves_ragged():

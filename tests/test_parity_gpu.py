@@ -163,8 +163,11 @@ def test_in_place_state_and_chaining():
     O1, _ = run_gpu(x1, 64, S0=state, S_final=state)
     O2, _ = run_gpu(x2, 64, S0=state, S_final=state)
     O_cat = torch.cat([O1, O2], dim=2)
-    assert rel_err(O_cat.cpu().numpy(), O_full.cpu().numpy()) < 1e-4
-    assert rel_err(state.cpu().numpy(), S_full.cpu().numpy()) < 1e-4
+    # the split moves chunk boundaries (different rounding): both results lie
+    # within the tolerance of the exact one
+    Or, Sr = run_oracle(x)
+    assert rel_err(O_cat.cpu().numpy(), Or) < TOL["bf16"]
+    assert rel_err(state.cpu().numpy(), Sr) < TOL["bf16"]
     check(x, O_full, S_full)
 
 
