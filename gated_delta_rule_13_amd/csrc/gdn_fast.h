@@ -34,12 +34,14 @@
 //                    its A blocks are from iteration i - 1)
 //            prep 1+ row strips of chunk i + 1: Gram and score tiles formed
 //                    into the diagonal blocks of A (fp32), the blocks below
-//                    them (fp16) and the masked decayed scores P (fp16); the
-//                    keys transposed (for the state update)
+//                    them (fp16) and the masked decayed scores P (fp16)
 //   phase B  scan    Y, V' = T_i Y, state update, O = diag(exp g) Z + P V'
 //            prep 0  decay vectors of chunk i + 2; diagonal solves of chunk i + 1
 //            prep 1+ keys and queries of chunk i + 2 into LDS (fp16)
 // The loop starts at i = -2 so that the first two iterations only prepare.
+// The state update reads K^T straight from the token-major key tile with
+// the LDS transposing read, so the keys stay three chunks deep (chunk i for
+// the scan, i + 1 for the strips, i + 2 being staged).
 #pragma once
 #include <type_traits>
 
@@ -63,34 +65,56 @@ __device__ __forceinline__ h8 cat_h(h4 a, h4 b) {
 __device__ __forceinline__ h4 to_h4(f32x4 x) { return __builtin_convertvector(x, h4); }
 __device__ __forceinline__ h4 zero_h4() { return h4{0, 0, 0, 0}; }
 
+typedef __attribute__((ext_vector_type(4))) short s4;
+typedef __attribute__((address_space(3))) const _Float16 lds_h;
+// An LDS address held in one register that the compiler may not split into
+// a base and a constant: reads at constant offsets from it then use the
+// instructions' 16-bit immediate offset, instead of one address register per
+// offset once the array lies beyond the immediate's reach.
+__device__ __forceinline__ lds_h* lds_opaque(const _Float16* p) {
+    lds_h* q = (lds_h*)p;
+    asm volatile("" : "+v"(q));
+    return q;
+}
+template <typename V>
+__device__ __forceinline__ V lds_at(lds_h* p, int off) {
+    return *reinterpret_cast<__attribute__((address_space(3))) const V*>(p + off);
+}
+// ds_read_b64_tr_b16: each lane addresses four consecutive 16-bit elements;
+// within each group of 16 lanes g, lane 16 g + i receives element i % 4 of
+// the four that lanes 16 g + 4 e + i / 4 (e = 0..3) addressed, in e order.
+__device__ __forceinline__ h4 lds_read_tr(lds_h* p) {
+    return __builtin_bit_cast(h4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                      (__attribute__((address_space(3))) s4*)p));
+}
+
 // Two bf16 (one 32-bit word) to two fp16.
 __device__ __forceinline__ unsigned bf2_to_h2(unsigned w) {
     const f2 f = {__builtin_bit_cast(float, w << 16), __builtin_bit_cast(float, w & 0xffff0000u)};
     return __builtin_bit_cast(unsigned, __builtin_convertvector(f, h2));
 }
 
-constexpr int kFastPrep = 4;
-
 template <int C, int DK, int NS, bool ETA>
 struct alignas(16) FastLds {
     static constexpr int NT = C / 16;                 // 16-token blocks per chunk
     static constexpr int NB = NT * (NT + 1) / 2;      // blocks on and below the diagonal
     static constexpr int NOFF = NT * (NT - 1) / 2;    // blocks below the diagonal
-    static constexpr int KP = DK + 8;                 // key / query row stride (fp16)
-    static constexpr int CP = C + 4;                  // transposed-key row stride (fp16)
+    // Strides chosen against the LDS banks (reads see 64 banks of 4 bytes,
+    // 16-byte reads served eight lanes from each half-wave at a time; writes
+    // see 32 banks, consecutive lanes together):
+    //   key / query rows DK + 16: the 16-byte operand reads of 8 rows by 2
+    //     lane groups cover all banks once, and the transposing reads of the
+    //     state update meet at most two to a bank;
+    //   16 x 16 blocks at row stride 20: conflict-free fp16 row writes;
+    //   the fp32 diagonal blocks of A get 4 floats between blocks, so the
+    //     solve's broadcast row reads of four blocks fall in distinct banks.
+    static constexpr int KP = DK + 16;                // key / query row stride (fp16)
     static constexpr int BP = 20;                     // row stride of 16 x 16 blocks
+    static constexpr int ADS = 16 * BP + 4;           // fp32 diagonal-block stride
     static constexpr int bidx(int b, int c) { return b * (b + 1) / 2 + c; }
     static constexpr int oidx(int b, int c) { return b * (b - 1) / 2 + c; }
-    // keys and queries by chunk parity; each 32-element block of a row in the
-    // scan's k-order (elements 4h..4h+3 then 16+4h..16+4h+3, h = 0..3), so an
-    // MFMA operand slice is one aligned 16-byte read
-    _Float16 K[2][C][KP];
-    _Float16 Q[2][C][KP];
-    _Float16 Kt[2][DK][CP];                    // keys transposed, natural token order
-    _Float16 Tb[2][NB][16][BP];                // T = (I - A)^{-1}, blocks (b, c <= b)
-    _Float16 Pb[2][NB][16][BP];                // masked decayed scores, blocks (b, c <= b)
-    _Float16 Ao[2][NOFF > 0 ? NOFF : 1][16][BP];   // A below the diagonal blocks
-    float Ad[2][NT][16][BP];                   // diagonal blocks of A (fp32, for the solve)
+    // Small arrays first: the scan reads them at fixed offsets that the LDS
+    // instructions' 16-bit immediate reaches from one lane base.
     // per-token vectors, three chunks live at a time
     float g2[3][C];    // inclusive cumsum of log2 alpha
     float er[3][C];    // 2^(g2_r - g2_ref): row factor of exp(g_r - g_i)
@@ -102,47 +126,93 @@ struct alignas(16) FastLds {
     float bge[ETA ? 3 : 1][ETA ? C : 4];   // beta exp(g)
     float glast[4];    // exp(g_last)
     int sep[4];        // row x column factors safe in fp32 for this chunk
+    _Float16 Tb[2][NB][16][BP];                // T = (I - A)^{-1}, blocks (b, c <= b)
+    _Float16 Pb[2][NB][16][BP];                // masked decayed scores, blocks (b, c <= b)
+    _Float16 Ao[2][NOFF > 0 ? NOFF : 1][16][BP];   // A below the diagonal blocks
+    float Ad[2][NT][ADS];                      // diagonal blocks of A (fp32, for the solve), rows BP apart
+    // keys by chunk modulo 3, queries by chunk parity; each 32-element block
+    // of a row in the scan's k-order (elements 4h..4h+3 then 16+4h..16+4h+3,
+    // h = 0..3), so an MFMA operand slice is one aligned 16-byte read
+    _Float16 K[3][C][KP];
+    _Float16 Q[2][C][KP];
 };
 
-// Row strips of the Gram / score formation: strip rt holds the tiles
-// (rt, ct) for ct = 0..rt of both A and the scores P, and the transposition
-// of key block rt.  Strips go to prep waves 1..3 so that the tile counts
-// balance: the last strip alone, the one before alone, the rest together.
-template <int NT>
-struct FastStrips {
-    static constexpr int owner(int rt) {
-        const int from_last = NT - 1 - rt;
-        return 1 + (from_last < 2 ? from_last : 2);
+// Prep waves per workgroup: six beside one or two scan waves, four beside
+// four (eight waves in all at most, two per SIMD).
+constexpr int fast_prep_waves(int ns) { return ns == 4 ? 4 : 6; }
+
+// Roles of the prep waves.  The waves of a workgroup are spread over the
+// four SIMDs of the compute unit so that waves w and w + 4 share one; the
+// roles are placed so that the two prep waves beside the scan waves (prep
+// waves 2 and 3 when there are six) carry the latency-bound, issue-light
+// jobs (the blocks of T below the diagonal, the decay vectors, the diagonal
+// solves) and the issue-heavy ones (Gram strips, staging) sit together on
+// the other two SIMDs.
+//   strips: row strip rt holds the tiles (rt, ct), ct = 0..rt, of both A and
+//           the scores P;
+//   stagers: convert and store the keys and queries of a chunk.
+template <int NS, int NT>
+struct FastRoles {
+    static constexpr int NP = fast_prep_waves(NS);
+    static constexpr int NSTG = NP == 6 ? 4 : 3;
+    static constexpr int toff_wave = NP == 6 ? 2 : 0;
+    static constexpr int vec_wave = NP == 6 ? 2 : 0;
+    static constexpr int solve_wave = NP == 6 ? 3 : 0;
+    static constexpr int stager(int pw) {
+        if (NP == 6) return pw == 0 ? 0 : pw == 1 ? 1 : pw == 4 ? 2 : pw == 5 ? 3 : -1;
+        return pw >= 1 ? pw - 1 : -1;
     }
-    static constexpr int count(int w) {
-        int n = 0;
-        for (int rt = 0; rt < NT; ++rt) n += owner(rt) == w;
-        return n;
-    }
-    // j-th strip of wave w, largest first
-    static constexpr int strip(int w, int j) {
-        for (int rt = NT - 1; rt >= 0; --rt)
-            if (owner(rt) == w) {
-                if (j == 0) return rt;
-                --j;
+    // Gram segments: (row strip rt, tile columns c0 <= ct < c1), encoded
+    // (rt << 16) | (c0 << 8) | c1, at most two per wave.  With six prep
+    // waves and four strips the 80 tile products split 24 / 16 / 16 / 24 so
+    // that the two SIMDs of the issue-heavy waves carry 40 each.
+    static constexpr int seg_code(int rt, int c0, int c1) { return (rt << 16) | (c0 << 8) | c1; }
+    static constexpr int seg(int w, int j) {
+        if (NP == 6) {
+            if (NT == 4) {
+                if (w == 0) return j == 0 ? seg_code(3, 0, 2) : j == 1 ? seg_code(0, 0, 1) : -1;
+                if (w == 1) return j == 0 ? seg_code(3, 2, 4) : -1;
+                if (w == 4) return j == 0 ? seg_code(1, 0, 2) : -1;
+                if (w == 5) return j == 0 ? seg_code(2, 0, 3) : -1;
+                return -1;
             }
-        return -1;
+            if (NT == 2) {
+                if (w == 0) return j == 0 ? seg_code(1, 0, 2) : -1;
+                if (w == 1) return j == 0 ? seg_code(0, 0, 1) : -1;
+                return -1;
+            }
+            return (w == 0 && j == 0) ? seg_code(0, 0, 1) : -1;
+        }
+        if (NT == 4) {
+            if (w == 1) return j == 0 ? seg_code(3, 0, 4) : -1;
+            if (w == 2) return j == 0 ? seg_code(2, 0, 3) : -1;
+            if (w == 3) return j == 0 ? seg_code(1, 0, 2) : j == 1 ? seg_code(0, 0, 1) : -1;
+            return -1;
+        }
+        if (NT == 2) {
+            if (w == 1) return j == 0 ? seg_code(1, 0, 2) : -1;
+            if (w == 2) return j == 0 ? seg_code(0, 0, 1) : -1;
+            return -1;
+        }
+        return (w == 1 && j == 0) ? seg_code(0, 0, 1) : -1;
     }
+    static constexpr int nseg(int w) { return seg(w, 0) < 0 ? 0 : seg(w, 1) < 0 ? 1 : 2; }
 };
 
 template <int C, int DK, int NS, bool ETA>
-__global__ __launch_bounds__((NS + kFastPrep) * 64) void gdn_fwd_fast_kernel(FwdParams p) {
-    constexpr int NP = kFastPrep;
+__global__ __launch_bounds__((NS + fast_prep_waves(NS)) * 64) void gdn_fwd_fast_kernel(FwdParams p) {
+    using R = FastRoles<NS, C / 16>;
+    constexpr int NP = R::NP;
     using L = FastLds<C, DK, NS, ETA>;
-    using ST = FastStrips<C / 16>;
     constexpr int NT = C / 16;
     constexpr int NK = DK / 16;              // 16-row tiles of S^T
     constexpr int NSS = DK / 32;             // k-steps over d_k
     constexpr int NTS = (C + 31) / 32;       // k-steps over the tokens of a chunk
     constexpr int DVT = 16 * NS;
     constexpr int KV = C * DK / 8;           // 16-byte vectors in a key tile
-    constexpr int NSTG = NP - 1;
+    constexpr int NSTG = R::NSTG;
     constexpr int NKV = (KV + 64 * NSTG - 1) / (64 * NSTG);
+    constexpr int BP_ = L::BP;
     static_assert(DK % 32 == 0 && C % 16 == 0, "shape");
     static_assert(sizeof(L) <= 160 * 1024, "LDS budget");
     __shared__ L s;
@@ -154,7 +224,8 @@ __global__ __launch_bounds__((NS + kFastPrep) * 64) void gdn_fwd_fast_kernel(Fwd
     const int h = lane >> 4;
     const bool scan = wave < NS;
     const int pw = wave - NS;
-    const int plane = tid - (NS + 1) * 64;   // 0..64*NSTG-1 on prep waves 1..NP-1
+    // staging lane 0..64*NSTG-1 on the stager waves
+    const int plane = (pw >= 0 ? R::stager(pw) : 0) * 64 + lane;
 
     int tile, bh;
     if (p.xcd_groups) {
@@ -200,23 +271,33 @@ __global__ __launch_bounds__((NS + kFastPrep) * 64) void gdn_fwd_fast_kernel(Fwd
                 }
             });
         };
-        // prep 1+: chunk cc's keys and queries into LDS as fp16, in k-order
+        // prep 1+: chunk cc's keys and queries into LDS as fp16, in k-order.
+        // The four lanes of a quad hold d_k 0..31 of one 32-element block,
+        // eight each; the pairs (q, q + 2) swap four elements so that every
+        // lane then holds one whole 16-byte k-order slice (d_k 4j..4j+3 and
+        // 16+4j..16+4j+3) and stores it with one write:
+        //   q = 0: d_k 0-3 + 16-19 at 0,  q = 1: 8-11 + 24-27 at 16,
+        //   q = 2: 4-7 + 20-23 at 8,      q = 3: 12-15 + 28-31 at 24.
         auto kq_store = [&](int cc) __attribute__((always_inline)) {
-            const int buf = cc & 1;
+            const int buf = cc & 1, kb3 = mod3(cc);
+            const int q = lane & 3;
+            const bool lo = q < 2;
+            auto swap2 = [](unsigned x) __attribute__((always_inline)) {
+                return (unsigned)__builtin_amdgcn_update_dpp(0, (int)x, 0x4E, 0xF, 0xF, false);
+            };
+            auto slice = [&](const uint4 v) __attribute__((always_inline)) {
+                const unsigned w0 = bf2_to_h2(v.x), w1 = bf2_to_h2(v.y), w2 = bf2_to_h2(v.z), w3 = bf2_to_h2(v.w);
+                const unsigned r0 = swap2(lo ? w2 : w0), r1 = swap2(lo ? w3 : w1);
+                return lo ? make_uint4(w0, w1, r0, r1) : make_uint4(r0, r1, w2, w3);
+            };
             static_for<0, NKV>([&](auto I) {
                 constexpr int i = decltype(I)::value;
                 const int vi = plane + i * 64 * NSTG;
                 if (i + 1 < NKV || vi < KV) {
                     const int r = vi / (DK / 8), c8 = (vi % (DK / 8)) * 8;
-                    const uint4 kv = stK[i], qv = stQ[i];
-                    *reinterpret_cast<uint2*>(&s.K[buf][r][kq_pos(c8)]) =
-                        make_uint2(bf2_to_h2(kv.x), bf2_to_h2(kv.y));
-                    *reinterpret_cast<uint2*>(&s.K[buf][r][kq_pos(c8 + 4)]) =
-                        make_uint2(bf2_to_h2(kv.z), bf2_to_h2(kv.w));
-                    *reinterpret_cast<uint2*>(&s.Q[buf][r][kq_pos(c8)]) =
-                        make_uint2(bf2_to_h2(qv.x), bf2_to_h2(qv.y));
-                    *reinterpret_cast<uint2*>(&s.Q[buf][r][kq_pos(c8 + 4)]) =
-                        make_uint2(bf2_to_h2(qv.z), bf2_to_h2(qv.w));
+                    const int pos = (c8 & ~31) + 16 * (q & 1) + 8 * (q >> 1);
+                    *reinterpret_cast<uint4*>(&s.K[kb3][r][pos]) = slice(stK[i]);
+                    *reinterpret_cast<uint4*>(&s.Q[buf][r][pos]) = slice(stQ[i]);
                 }
             });
         };
@@ -260,86 +341,77 @@ __global__ __launch_bounds__((NS + kFastPrep) * 64) void gdn_fwd_fast_kernel(Fwd
                 s.sep[vb3] = (g0 - gl) <= 96.f;
             }
         };
-        // prep 1+: the row strips of chunk cc owned by this wave.  Strip rt:
-        // key block rt (B operand of A's tiles), query block rt (B operand
-        // of the scores) and each key block ct <= rt (A operand of both) are
-        // read from LDS once; then the tiles are formed,
+        // Gram segments of chunk cc owned by this wave.  Segment (rt, c0, c1):
+        // key block rt (B operand of A's tiles), query block rt (B operand of
+        // the scores) and each key block ct in [c0, c1) (A operand of both)
+        // are read from LDS once; then the tiles are formed,
         //   A_ri = -beta_r exp(g_r - g_i) k_r.k_i (i < r),  P_ri = exp(g_r - g_i) q_r.k_i (i <= r),
         // with lane (n, h) holding row r = 16 rt + n, columns 16 ct + 4 h + e.
-        // The same key block is transposed into Kt by MFMAs against 0/1
-        // selectors: with A the key rows of a 16 x 32 slice and B selecting
-        // slice element 16 u + n', lane (n', h) receives tokens 4h..4h+3 at
-        // dimension 16 u + n' -- four consecutive tokens of one row of K^T
-        // (exact: one product with 1 per output).
         auto strips = [&](auto W, int cc) __attribute__((always_inline)) {
             constexpr int w = decltype(W)::value;
             const int buf = cc & 1;
             const int vb3 = mod3(cc);
-            // element e of lane (n, h) in the k-order stands for slice position
-            // pos(e) = e < 4 ? 4h + e : 16 + 4h + e - 4
-            h8 sel0, sel1;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int pos = e < 4 ? 4 * h + e : 16 + 4 * h + (e - 4);
-                sel0[e] = (_Float16)(pos == n ? 1.f : 0.f);
-                sel1[e] = (_Float16)(pos == 16 + n ? 1.f : 0.f);
-            }
             const bool sep = s.sep[vb3];
-            static_for<0, ST::count(w)>([&](auto JJ) {
-                constexpr int rt = ST::strip(w, decltype(JJ)::value);
+            static_for<0, R::nseg(w)>([&](auto JJ) {
+                constexpr int code = R::seg(w, decltype(JJ)::value);
+                constexpr int rt = code >> 16, c0 = (code >> 8) & 255, c1 = code & 255;
                 const int r = 16 * rt + n;
                 h8 kb[NSS], qb[NSS];
 #pragma unroll
                 for (int ss = 0; ss < NSS; ++ss) {
-                    kb[ss] = *reinterpret_cast<const h8*>(&s.K[buf][r][32 * ss + 8 * h]);
+                    kb[ss] = *reinterpret_cast<const h8*>(&s.K[vb3][r][32 * ss + 8 * h]);
                     qb[ss] = *reinterpret_cast<const h8*>(&s.Q[buf][r][32 * ss + 8 * h]);
                 }
                 const float nbr = -s.beta[vb3][r];
                 const float g2r = s.g2[vb3][r];
                 const float err = s.er[vb3][r];
-                static_for<0, rt + 1>([&](auto CC) {
+                // every product of the strip before any store: LDS stores
+                // would keep the compiler from hoisting the next tile's loads
+                f32x4 ga[NT], gp[NT];
+                static_for<c0, c1>([&](auto CC) {
                     constexpr int ct = decltype(CC)::value;
                     h8 ka[NSS];
 #pragma unroll
                     for (int ss = 0; ss < NSS; ++ss) {
                         if constexpr (ct == rt) ka[ss] = kb[ss];
-                        else ka[ss] = *reinterpret_cast<const h8*>(&s.K[buf][16 * ct + n][32 * ss + 8 * h]);
+                        else ka[ss] = *reinterpret_cast<const h8*>(&s.K[vb3][16 * ct + n][32 * ss + 8 * h]);
                     }
-                    f32x4 ga = zero4(), gp = zero4();
+                    ga[ct] = zero4();
+                    gp[ct] = zero4();
 #pragma unroll
                     for (int ss = 0; ss < NSS; ++ss) {
-                        ga = mfma_h(ka[ss], kb[ss], ga);
-                        gp = mfma_h(ka[ss], qb[ss], gp);
+                        ga[ct] = mfma_h(ka[ss], kb[ss], ga[ct]);
+                        gp[ct] = mfma_h(ka[ss], qb[ss], gp[ct]);
                     }
+                });
+                f32x4 fic[NT], g2c[NT];
+                static_for<c0, c1>([&](auto CC) {
+                    constexpr int ct = decltype(CC)::value;
+                    fic[ct] = *reinterpret_cast<const f32x4*>(&s.fi[vb3][16 * ct + 4 * h]);
+                    g2c[ct] = *reinterpret_cast<const f32x4*>(&s.g2[vb3][16 * ct + 4 * h]);
+                });
+                static_for<c0, c1>([&](auto CC) {
+                    constexpr int ct = decltype(CC)::value;
                     const int i0 = 16 * ct + 4 * h;
                     f32x4 d;
                     if (sep) {
-                        d = err * *reinterpret_cast<const f32x4*>(&s.fi[vb3][i0]);
+                        d = err * fic[ct];
                     } else {
-                        const f32x4 g2i = *reinterpret_cast<const f32x4*>(&s.g2[vb3][i0]);
 #pragma unroll
-                        for (int e = 0; e < 4; ++e) d[e] = __builtin_amdgcn_exp2f(g2r - g2i[e]);
+                        for (int e = 0; e < 4; ++e) d[e] = __builtin_amdgcn_exp2f(g2r - g2c[ct][e]);
                     }
                     f32x4 va, vp;
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
-                        va[e] = (ct < rt || i0 + e < r) ? nbr * d[e] * ga[e] : 0.f;
-                        vp[e] = (ct < rt || i0 + e <= r) ? d[e] * gp[e] : 0.f;
+                        va[e] = (ct < rt || i0 + e < r) ? nbr * d[e] * ga[ct][e] : 0.f;
+                        vp[e] = (ct < rt || i0 + e <= r) ? d[e] * gp[ct][e] : 0.f;
                     }
                     *reinterpret_cast<h4*>(&s.Pb[buf][L::bidx(rt, ct)][n][4 * h]) = to_h4(vp);
                     if constexpr (ct == rt)
-                        *reinterpret_cast<f32x4*>(&s.Ad[buf][rt][n][4 * h]) = va;
+                        *reinterpret_cast<f32x4*>(&s.Ad[buf][rt][n * BP_ + 4 * h]) = va;
                     else
                         *reinterpret_cast<h4*>(&s.Ao[buf][L::oidx(rt, ct)][n][4 * h]) = to_h4(va);
                 });
-                // key block rt transposed
-#pragma unroll
-                for (int ss = 0; ss < NSS; ++ss) {
-                    const f32x4 d0 = mfma_h(kb[ss], sel0, zero4());
-                    const f32x4 d1 = mfma_h(kb[ss], sel1, zero4());
-                    *reinterpret_cast<h4*>(&s.Kt[buf][32 * ss + n][16 * rt + 4 * h]) = to_h4(d0);
-                    *reinterpret_cast<h4*>(&s.Kt[buf][32 * ss + 16 + n][16 * rt + 4 * h]) = to_h4(d1);
-                }
             });
         };
         // prep 0: T_bb = (I - A_bb)^{-1} for all diagonal blocks of chunk cc:
@@ -359,7 +431,7 @@ __global__ __launch_bounds__((NS + kFastPrep) * 64) void gdn_fwd_fast_kernel(Fwd
                     constexpr int m = decltype(M)::value;
 #pragma unroll
                     for (int q = 0; 4 * q < m; ++q)
-                        abuf[m % 3][q] = *reinterpret_cast<const f32x4*>(&s.Ad[buf][b][m][4 * q]);
+                        abuf[m % 3][q] = *reinterpret_cast<const f32x4*>(&s.Ad[buf][b][m * BP_ + 4 * q]);
                 };
                 load_row(std::integral_constant<int, 15>{});
                 load_row(std::integral_constant<int, 14>{});
@@ -389,19 +461,25 @@ __global__ __launch_bounds__((NS + kFastPrep) * 64) void gdn_fwd_fast_kernel(Fwd
         auto t_off = [&](int cc) __attribute__((always_inline)) {
             if constexpr (NT > 1) {
                 const int buf = cc & 1;
-                h4 Tr[NT][NT];
-                // column n, rows 4h..4h+3 of a diagonal block of T
-                auto diag_col = [&](int c) __attribute__((always_inline)) {
-                    h4 v;
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) v[j] = s.Tb[buf][L::bidx(c, c)][4 * h + j][n];
-                    return v;
-                };
-                h4 Tdiag[NT];
+                // all operands first (LDS stores below would keep later loads
+                // from being hoisted): the A blocks below the diagonal, the
+                // rows of each T_bb (A operand) and the columns of each T_cc
+                // (B operand, lane (n, h): rows 4h..4h+3 of column n)
+                h4 Ab[NT][NT], Trow[NT], Tcol[NT];
+                static_for<1, NT>([&](auto BB) {
+                    constexpr int b = decltype(BB)::value;
+                    static_for<0, b>([&](auto KK) {
+                        constexpr int k = decltype(KK)::value;
+                        Ab[b][k] = *reinterpret_cast<const h4*>(&s.Ao[buf][L::oidx(b, k)][n][4 * h]);
+                    });
+                    Trow[b] = *reinterpret_cast<const h4*>(&s.Tb[buf][L::bidx(b, b)][n][4 * h]);
+                });
                 static_for<0, NT - 1>([&](auto CC) {
                     constexpr int c = decltype(CC)::value;
-                    Tdiag[c] = diag_col(c);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) Tcol[c][j] = s.Tb[buf][L::bidx(c, c)][4 * h + j][n];
                 });
+                h4 Tr[NT][NT];
                 static_for<1, NT>([&](auto DD) {
                     constexpr int d = decltype(DD)::value;
                     static_for<0, NT - d>([&](auto CC) {
@@ -410,20 +488,24 @@ __global__ __launch_bounds__((NS + kFastPrep) * 64) void gdn_fwd_fast_kernel(Fwd
                         f32x4 R = zero4();
                         static_for<0, (d + 1) / 2>([&](auto KK) {
                             constexpr int k = c + 2 * decltype(KK)::value;
-                            const h4 a0 = *reinterpret_cast<const h4*>(&s.Ao[buf][L::oidx(b, k)][n][4 * h]);
                             h4 t0;
-                            if constexpr (k == c) t0 = Tdiag[c];
+                            if constexpr (k == c) t0 = Tcol[c];
                             else t0 = Tr[k][c];
                             h4 a1 = zero_h4(), t1 = zero_h4();
                             if constexpr (k + 1 < b) {
-                                a1 = *reinterpret_cast<const h4*>(&s.Ao[buf][L::oidx(b, k + 1)][n][4 * h]);
+                                a1 = Ab[b][k + 1];
                                 t1 = Tr[k + 1][c];
                             }
-                            R = mfma_h(cat_h(a0, a1), cat_h(t0, t1), R);
+                            R = mfma_h(cat_h(Ab[b][k], a1), cat_h(t0, t1), R);
                         });
-                        const h4 tbb = *reinterpret_cast<const h4*>(&s.Tb[buf][L::bidx(b, b)][n][4 * h]);
-                        const f32x4 tbc = mfma_h(cat_h(tbb, zero_h4()), cat_h(to_h4(R), zero_h4()), zero4());
+                        const f32x4 tbc = mfma_h(cat_h(Trow[b], zero_h4()), cat_h(to_h4(R), zero_h4()), zero4());
                         Tr[b][c] = to_h4(tbc);
+                    });
+                });
+                static_for<1, NT>([&](auto BB) {
+                    constexpr int b = decltype(BB)::value;
+                    static_for<0, b>([&](auto CC) {
+                        constexpr int c = decltype(CC)::value;
 #pragma unroll
                         for (int j = 0; j < 4; ++j) s.Tb[buf][L::bidx(b, c)][4 * h + j][n] = Tr[b][c][j];
                     });
@@ -447,10 +529,10 @@ __global__ __launch_bounds__((NS + kFastPrep) * 64) void gdn_fwd_fast_kernel(Fwd
 
         auto prep_role = [&](auto W) __attribute__((always_inline)) {
             constexpr int w = decltype(W)::value;
+            constexpr bool stg = R::stager(w) >= 0;
             auto step = [&](auto PAR, int i) __attribute__((always_inline)) {
-                constexpr int par = decltype(PAR)::value;   // parity of i
                 // ---- phase A ----
-                if constexpr (w == 0) {
+                if constexpr (w == R::toff_wave) {
                     if (i >= 0) {
                         t_off(i);
                         if (p.dbg_T) {
@@ -458,18 +540,22 @@ __global__ __launch_bounds__((NS + kFastPrep) * 64) void gdn_fwd_fast_kernel(Fwd
                             dbg_t(i);
                         }
                     }
-                } else {
+                }
+                if constexpr (R::nseg(w) > 0) {
                     if (i + 1 >= 0 && i + 1 < nchunks) strips(W, i + 1);
                 }
                 __syncthreads();
                 // ---- phase B ----
-                if constexpr (w == 0) {
+                if constexpr (w == R::vec_wave) {
                     if (i + 2 < nchunks) {
                         vectors(i + 2);
                         if (i + 3 < nchunks) gate_load(i + 3);
                     }
+                }
+                if constexpr (w == R::solve_wave) {
                     if (i + 1 >= 0 && i + 1 < nchunks) diag_solve(i + 1);
-                } else {
+                }
+                if constexpr (stg) {
                     if (i + 2 < nchunks) {
                         kq_store(i + 2);
                         if (i + 3 < nchunks) kq_load(i + 3);
@@ -477,8 +563,8 @@ __global__ __launch_bounds__((NS + kFastPrep) * 64) void gdn_fwd_fast_kernel(Fwd
                 }
                 __syncthreads();
             };
-            if constexpr (w == 0) gate_load(0);
-            else kq_load(0);
+            if constexpr (w == R::vec_wave) gate_load(0);
+            if constexpr (stg) kq_load(0);
             for (int i = -2; i < nchunks; i += 2) {
                 step(std::integral_constant<int, 0>{}, i);
                 if (i + 1 < nchunks) step(std::integral_constant<int, 1>{}, i + 1);
@@ -488,7 +574,9 @@ __global__ __launch_bounds__((NS + kFastPrep) * 64) void gdn_fwd_fast_kernel(Fwd
             case 0: prep_role(std::integral_constant<int, 0>{}); break;
             case 1: prep_role(std::integral_constant<int, 1>{}); break;
             case 2: prep_role(std::integral_constant<int, 2>{}); break;
-            default: prep_role(std::integral_constant<int, 3>{}); break;
+            case 3: prep_role(std::integral_constant<int, 3>{}); break;
+            case 4: if constexpr (NP > 4) prep_role(std::integral_constant<int, 4>{}); break;
+            default: if constexpr (NP > 5) prep_role(std::integral_constant<int, 5>{}); break;
         }
     } else {
         // ============================== scan ===============================
@@ -530,7 +618,7 @@ __global__ __launch_bounds__((NS + kFastPrep) * 64) void gdn_fwd_fast_kernel(Fwd
         auto pair_op = [&](const f32x4* tiles, int sidx) __attribute__((always_inline)) {
             return cat_h(to_h4(tiles[2 * sidx]), 2 * sidx + 1 < NT ? to_h4(tiles[2 * sidx + 1]) : zero_h4());
         };
-        // one chunk; PAR = parity of c (the LDS buffer of K, Q, Kt, T and P)
+        // one chunk; PAR = parity of c (the LDS buffer of Q, T and P; keys by c mod 3)
         auto chunk = [&](auto PAR, int c) __attribute__((always_inline)) {
             constexpr int buf = decltype(PAR)::value;
             const int vb3 = c % 3;
@@ -542,30 +630,53 @@ __global__ __launch_bounds__((NS + kFastPrep) * 64) void gdn_fwd_fast_kernel(Fwd
             f32x4 X[NT], Zt[NT];
 #pragma unroll
             for (int rt = 0; rt < NT; ++rt) { X[rt] = zero4(); Zt[rt] = zero4(); }
+            lds_h* kl = lds_opaque(&s.K[vb3][n][8 * h]);
+            lds_h* ql = lds_opaque(&s.Q[buf][n][8 * h]);
 #pragma unroll
             for (int ss = 0; ss < NSS; ++ss) {
                 h8 kf[NT], qf[NT];
 #pragma unroll
                 for (int rt = 0; rt < NT; ++rt) {
-                    kf[rt] = *reinterpret_cast<const h8*>(&s.K[buf][16 * rt + n][32 * ss + 8 * h]);
-                    qf[rt] = *reinterpret_cast<const h8*>(&s.Q[buf][16 * rt + n][32 * ss + 8 * h]);
+                    kf[rt] = lds_at<h8>(kl, 16 * rt * L::KP + 32 * ss);
+                    qf[rt] = lds_at<h8>(ql, 16 * rt * L::KP + 32 * ss);
                 }
 #pragma unroll
                 for (int rt = 0; rt < NT; ++rt) X[rt] = mfma_h(kf[rt], sh[ss], X[rt]);
 #pragma unroll
                 for (int rt = 0; rt < NT; ++rt) Zt[rt] = mfma_h(sh[ss], qf[rt], Zt[rt]);
             }
-            // per-token vectors of chunk c for phase B (in LDS since an
-            // iteration ago): read now, so that their latency hides behind the
-            // products above
+            // The right-hand side needs X and the values only: it is formed in
+            // this phase, where the scan waves wait for the prep waves anyway,
+            // and only its fp16 operand crosses the barrier.
+            // This chunk's values in the accumulator layout (token 16 rt + 4 h + j, column n):
+            f32x4 Vt[NT];
+#pragma unroll
+            for (int rt = 0; rt < NT; ++rt)
+                Vt[rt] = mfma_bf16(__builtin_bit_cast(bf16x8, vraw[rt]), vsel, zero4());
+            // the next chunk's values (past the last chunk every row lies
+            // outside the buffer and reads zero; loading unconditionally keeps
+            // the wait for them precise)
+            v_load(c + 1);
+            // Y = diag(beta) (V - diag(exp g) X)  (or eta V - beta exp(g) X)
             const float* f1b = ETA ? &s.eta[vb3][0] : &s.beta[vb3][0];
             const float* f2b = ETA ? &s.bge[vb3][0] : &s.eg[vb3][0];
-            f32x4 f1[NT], f2[NT], fd[NT];
+            f32x4 Y[NT];
+#pragma unroll
+            for (int rt = 0; rt < NT; ++rt) {
+                const f32x4 f1 = *reinterpret_cast<const f32x4*>(f1b + 16 * rt + 4 * h);
+                const f32x4 f2 = *reinterpret_cast<const f32x4*>(f2b + 16 * rt + 4 * h);
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    Y[rt][j] = ETA ? f1[j] * Vt[rt][j] - f2[j] * X[rt][j] : f1[j] * (Vt[rt][j] - f2[j] * X[rt][j]);
+            }
+            h8 yh[NTS];
+#pragma unroll
+            for (int ss = 0; ss < NTS; ++ss) yh[ss] = pair_op(Y, ss);
+            // factors of phase B
+            f32x4 fd[NT];
             float egr[NT];
 #pragma unroll
             for (int rt = 0; rt < NT; ++rt) {
-                f1[rt] = *reinterpret_cast<const f32x4*>(f1b + 16 * rt + 4 * h);
-                f2[rt] = *reinterpret_cast<const f32x4*>(f2b + 16 * rt + 4 * h);
                 fd[rt] = *reinterpret_cast<const f32x4*>(&s.dec[vb3][16 * rt + 4 * h]);
                 egr[rt] = s.eg[vb3][16 * rt + n];
             }
@@ -585,23 +696,27 @@ __global__ __launch_bounds__((NS + kFastPrep) * 64) void gdn_fwd_fast_kernel(Fwd
                     top[b][sidx] = cat_h(t0_, t1_);
                 });
             });
-            // this chunk's values in the accumulator layout (token 16 rt + 4 h + j, column n)
-            f32x4 Vt[NT];
+            // K^T operands of the state update, by the transposing read of the
+            // token-major keys: for d_k block t and token k-step ss, lane
+            // (n, h) receives d_k 16 t + n at the k-slots of the update's
+            // other operand (tokens 32 ss + 4 h + j, then 32 ss + 16 + 4 h + j);
+            // the lane addressing them, 16 h + 4 e + m, points at token
+            // 32 ss + 4 h + e (+ 16) and d_k 16 t + 4 m .. + 3, whose place in
+            // the row's k-order is 32 (t / 2) + 8 m + 4 (t % 2).  The first
+            // token k-step is read now, well ahead of its use, so that its
+            // latency hides behind the products in between; the second is read
+            // into the same registers as the first is consumed.
+            h8 ktop[NK];
+            lds_h* ktr = lds_opaque(&s.K[vb3][4 * h + ((lane >> 2) & 3)][8 * (lane & 3)]);
+            auto kt_one = [&](int ss, int t) __attribute__((always_inline)) {
+                lds_h* a = ktr + 32 * ss * L::KP + 32 * (t >> 1) + 4 * (t & 1);
+                const h4 lo = lds_read_tr(a);
+                const h4 hi = 32 * ss + 16 < C ? lds_read_tr(a + 16 * L::KP) : zero_h4();
+                return cat_h(lo, hi);
+            };
 #pragma unroll
-            for (int rt = 0; rt < NT; ++rt)
-                Vt[rt] = mfma_bf16(__builtin_bit_cast(bf16x8, vraw[rt]), vsel, zero4());
-            if (c + 1 < nchunks) v_load(c + 1);
-            // right-hand side Y = diag(beta) (V - diag(exp g) X)  (or eta V - beta exp(g) X)
-            f32x4 Y[NT];
-#pragma unroll
-            for (int rt = 0; rt < NT; ++rt)
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    Y[rt][j] = ETA ? f1[rt][j] * Vt[rt][j] - f2[rt][j] * X[rt][j]
-                                   : f1[rt][j] * (Vt[rt][j] - f2[rt][j] * X[rt][j]);
-            h8 yh[NTS];
-#pragma unroll
-            for (int ss = 0; ss < NTS; ++ss) yh[ss] = pair_op(Y, ss);
+            for (int t = 0; t < NK; ++t) ktop[t] = kt_one(0, t);
+            __builtin_amdgcn_sched_barrier(0);
             // V' = T Y (T lower block triangular: row block b uses k-steps s <= b / 2)
             f32x4 Vp[NT];
             static_for<0, NT>([&](auto BB) {
@@ -642,19 +757,12 @@ __global__ __launch_bounds__((NS + kFastPrep) * 64) void gdn_fwd_fast_kernel(Fwd
 #pragma unroll
             for (int t = 0; t < NK; ++t) Sacc[t] *= gl;
 #pragma unroll
-            for (int ss = 0; ss < NTS; ++ss) {
-                h8 kt[NK];
+            for (int ss = 0; ss < NTS; ++ss)
 #pragma unroll
                 for (int t = 0; t < NK; ++t) {
-                    const _Float16* row = &s.Kt[buf][16 * t + n][0];
-                    const h4 a = *reinterpret_cast<const h4*>(row + 32 * ss + 4 * h);
-                    const h4 b = 32 * ss + 16 < C ? *reinterpret_cast<const h4*>(row + 32 * ss + 16 + 4 * h)
-                                                  : zero_h4();
-                    kt[t] = cat_h(a, b);
+                    Sacc[t] = mfma_h(ktop[t], vd[ss], Sacc[t]);
+                    if (ss + 1 < NTS) ktop[t] = kt_one(ss + 1, t);
                 }
-#pragma unroll
-                for (int t = 0; t < NK; ++t) Sacc[t] = mfma_h(kt[t], vd[ss], Sacc[t]);
-            }
             // O^T = diag(exp g) Z^T + V'^T P^T  (lane: row 16 rt + n, columns 4h..4h+3);
             // output rows past the end of the sequence fall outside the buffer (dropped)
             static_for<0, NT>([&](auto RR) {

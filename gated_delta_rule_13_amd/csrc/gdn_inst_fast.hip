@@ -15,7 +15,7 @@ namespace {
 template <int NS, bool ETA>
 void launch(const FwdParams& p, long nblocks, hipStream_t st) {
     hipLaunchKernelGGL((gdn_fwd_fast_kernel<GDN_C, GDN_DK, NS, ETA>), dim3((unsigned)nblocks),
-                       dim3((NS + kFastPrep) * 64), 0, st, p);
+                       dim3((NS + fast_prep_waves(NS)) * 64), 0, st, p);
 }
 }  // namespace
 
