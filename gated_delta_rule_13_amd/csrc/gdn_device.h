@@ -46,6 +46,10 @@ __device__ __forceinline__ uint32_t buf_load_bf16_bits(buf_t r, uint32_t off) {
     return (uint32_t)(unsigned short)__builtin_amdgcn_raw_buffer_load_b16(r, (int)off, 0, 0);
 }
 __device__ __forceinline__ float bf16_bits_to_float(uint32_t b) { return __builtin_bit_cast(float, b << 16); }
+__device__ __forceinline__ uint2 buf_load_8B(buf_t r, uint32_t off) {
+    const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0);
+    return make_uint2(v[0], v[1]);
+}
 __device__ __forceinline__ uint4 buf_load_16B(buf_t r, uint32_t off) {
     const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
     return make_uint4(v[0], v[1], v[2], v[3]);

@@ -258,46 +258,39 @@ __global__ __launch_bounds__((NS + fast_prep_waves(NS)) * 64) void gdn_fwd_fast_
         float stA = 1.f, stB = 0.f, stE = 0.f;  // prep 0: gates of the next chunk to prepare
 
         // prep 1+: global loads of chunk cc's keys and queries (rows past the
-        // end of the sequence read as zero)
+        // end of the sequence read as zero).  Staging vector vi is the 16-byte
+        // k-order slice u = vi % (DK / 8) of row vi / (DK / 8): d_k
+        // 32 (u / 4) + 4 (u % 4) .. + 3 and the four 16 further on, fetched as
+        // two 8-byte pieces so that no lane exchange is needed.
         auto kq_load = [&](int cc) __attribute__((always_inline)) {
             const int t0 = cc * C;
             static_for<0, NKV>([&](auto I) {
                 constexpr int i = decltype(I)::value;
                 const int vi = plane + i * 64 * NSTG;
                 if (i + 1 < NKV || vi < KV) {
-                    const int r = vi / (DK / 8), c8 = (vi % (DK / 8)) * 8;
-                    stK[i] = buf_load_16B(kbuf, 2u * ((t0 + r) * DK + c8));
-                    stQ[i] = buf_load_16B(qbuf, 2u * ((t0 + r) * DK + c8));
+                    const int r = vi / (DK / 8), u = vi % (DK / 8);
+                    const uint32_t off = 2u * ((t0 + r) * DK + 32 * (u >> 2) + 4 * (u & 3));
+                    const uint2 k0 = buf_load_8B(kbuf, off), k1 = buf_load_8B(kbuf, off + 32);
+                    const uint2 q0 = buf_load_8B(qbuf, off), q1 = buf_load_8B(qbuf, off + 32);
+                    stK[i] = make_uint4(k0.x, k0.y, k1.x, k1.y);
+                    stQ[i] = make_uint4(q0.x, q0.y, q1.x, q1.y);
                 }
             });
         };
-        // prep 1+: chunk cc's keys and queries into LDS as fp16, in k-order.
-        // The four lanes of a quad hold d_k 0..31 of one 32-element block,
-        // eight each; the pairs (q, q + 2) swap four elements so that every
-        // lane then holds one whole 16-byte k-order slice (d_k 4j..4j+3 and
-        // 16+4j..16+4j+3) and stores it with one write:
-        //   q = 0: d_k 0-3 + 16-19 at 0,  q = 1: 8-11 + 24-27 at 16,
-        //   q = 2: 4-7 + 20-23 at 8,      q = 3: 12-15 + 28-31 at 24.
+        // prep 1+: chunk cc's keys and queries into LDS as fp16, one k-order
+        // slice per staging vector
         auto kq_store = [&](int cc) __attribute__((always_inline)) {
             const int buf = cc & 1, kb3 = mod3(cc);
-            const int q = lane & 3;
-            const bool lo = q < 2;
-            auto swap2 = [](unsigned x) __attribute__((always_inline)) {
-                return (unsigned)__builtin_amdgcn_update_dpp(0, (int)x, 0x4E, 0xF, 0xF, false);
-            };
             auto slice = [&](const uint4 v) __attribute__((always_inline)) {
-                const unsigned w0 = bf2_to_h2(v.x), w1 = bf2_to_h2(v.y), w2 = bf2_to_h2(v.z), w3 = bf2_to_h2(v.w);
-                const unsigned r0 = swap2(lo ? w2 : w0), r1 = swap2(lo ? w3 : w1);
-                return lo ? make_uint4(w0, w1, r0, r1) : make_uint4(r0, r1, w2, w3);
+                return make_uint4(bf2_to_h2(v.x), bf2_to_h2(v.y), bf2_to_h2(v.z), bf2_to_h2(v.w));
             };
             static_for<0, NKV>([&](auto I) {
                 constexpr int i = decltype(I)::value;
                 const int vi = plane + i * 64 * NSTG;
                 if (i + 1 < NKV || vi < KV) {
-                    const int r = vi / (DK / 8), c8 = (vi % (DK / 8)) * 8;
-                    const int pos = (c8 & ~31) + 16 * (q & 1) + 8 * (q >> 1);
-                    *reinterpret_cast<uint4*>(&s.K[kb3][r][pos]) = slice(stK[i]);
-                    *reinterpret_cast<uint4*>(&s.Q[buf][r][pos]) = slice(stQ[i]);
+                    const int r = vi / (DK / 8), u = vi % (DK / 8);
+                    *reinterpret_cast<uint4*>(&s.K[kb3][r][8 * u]) = slice(stK[i]);
+                    *reinterpret_cast<uint4*>(&s.Q[buf][r][8 * u]) = slice(stQ[i]);
                 }
             });
         };
@@ -728,22 +721,20 @@ __global__ __launch_bounds__((NS + fast_prep_waves(NS)) * 64) void gdn_fwd_fast_
                 });
                 Vp[b] = acc;
             });
-            if (p.dbg_V) {
-                // stage output: V' rows of this chunk (rows past the end of the
-                // sequence fall outside the buffer and are dropped)
-                const buf_t dbuf = buffer_over(p.dbg_V + (size_t)bh * T * dv, (uint32_t)T * dv * 4);
-                const uint32_t lane_off = 4u * ((uint32_t)(t0 + 4 * h) * dv + col0 + n);
-#pragma unroll
-                for (int rt = 0; rt < NT; ++rt)
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        // (a bit_cast of the vector component itself stored
-                        // component 0 four times; copy it out first)
-                        const float e = Vp[rt][j];
-                        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(e), dbuf, (int)lane_off,
-                                                              (int)(4u * (16 * rt + j) * dv), 0);
-                    }
-            }
+            // the scores of this chunk, read now (T's registers are free) so
+            // that their latency hides behind the state update
+            h8 pf[NT][NTS];
+            static_for<0, NT>([&](auto RR) {
+                constexpr int rt = decltype(RR)::value;
+                static_for<0, rt / 2 + 1>([&](auto SS) {
+                    constexpr int sidx = decltype(SS)::value;
+                    const h4 p0 = *reinterpret_cast<const h4*>(&s.Pb[buf][L::bidx(rt, 2 * sidx)][n][4 * h]);
+                    h4 p1 = zero_h4();
+                    if constexpr (2 * sidx + 1 <= rt)
+                        p1 = *reinterpret_cast<const h4*>(&s.Pb[buf][L::bidx(rt, 2 * sidx + 1)][n][4 * h]);
+                    pf[rt][sidx] = cat_h(p0, p1);
+                });
+            });
             h8 vh[NTS];
 #pragma unroll
             for (int ss = 0; ss < NTS; ++ss) vh[ss] = pair_op(Vp, ss);
@@ -763,24 +754,45 @@ __global__ __launch_bounds__((NS + fast_prep_waves(NS)) * 64) void gdn_fwd_fast_
                     Sacc[t] = mfma_h(ktop[t], vd[ss], Sacc[t]);
                     if (ss + 1 < NTS) ktop[t] = kt_one(ss + 1, t);
                 }
-            // O^T = diag(exp g) Z^T + V'^T P^T  (lane: row 16 rt + n, columns 4h..4h+3);
-            // output rows past the end of the sequence fall outside the buffer (dropped)
+            // O^T = diag(exp g) Z^T + V'^T P^T  (lane: row 16 rt + n, columns 4h..4h+3):
+            // all products first, then the stores under one branch on the
+            // output type; output rows past the end of the sequence fall
+            // outside the buffer (dropped)
+            f32x4 o[NT];
             static_for<0, NT>([&](auto RR) {
                 constexpr int rt = decltype(RR)::value;
                 f32x4 acc = zero4();
                 static_for<0, rt / 2 + 1>([&](auto SS) {
                     constexpr int sidx = decltype(SS)::value;
-                    const h4 p0 = *reinterpret_cast<const h4*>(&s.Pb[buf][L::bidx(rt, 2 * sidx)][n][4 * h]);
-                    h4 p1 = zero_h4();
-                    if constexpr (2 * sidx + 1 <= rt)
-                        p1 = *reinterpret_cast<const h4*>(&s.Pb[buf][L::bidx(rt, 2 * sidx + 1)][n][4 * h]);
-                    acc = mfma_h(vh[sidx], cat_h(p0, p1), acc);
+                    acc = mfma_h(vh[sidx], pf[rt][sidx], acc);
                 });
-                const f32x4 o = egr[rt] * Zt[rt] + acc;
-                const uint32_t row = (uint32_t)(t0 + 16 * rt + n) * dv + col0 + 4 * h;
-                if (p.o_bf16) buf_store(obuf, row * 2, __builtin_convertvector(o, bf16x4));
-                else buf_store(obuf, row * 4, o);
+                o[rt] = egr[rt] * Zt[rt] + acc;
             });
+            const uint32_t row0 = (uint32_t)(t0 + n) * dv + col0 + 4 * h;
+            if (p.o_bf16) {
+#pragma unroll
+                for (int rt = 0; rt < NT; ++rt)
+                    buf_store(obuf, (row0 + 16u * rt * dv) * 2, __builtin_convertvector(o[rt], bf16x4));
+            } else {
+#pragma unroll
+                for (int rt = 0; rt < NT; ++rt) buf_store(obuf, (row0 + 16u * rt * dv) * 4, o[rt]);
+            }
+            if (p.dbg_V) {
+                // stage output: V' rows of this chunk (rows past the end of the
+                // sequence fall outside the buffer and are dropped)
+                const buf_t dbuf = buffer_over(p.dbg_V + (size_t)bh * T * dv, (uint32_t)T * dv * 4);
+                const uint32_t lane_off = 4u * ((uint32_t)(t0 + 4 * h) * dv + col0 + n);
+#pragma unroll
+                for (int rt = 0; rt < NT; ++rt)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        // (a bit_cast of the vector component itself stored
+                        // component 0 four times; copy it out first)
+                        const float e = Vp[rt][j];
+                        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(e), dbuf, (int)lane_off,
+                                                              (int)(4u * (16 * rt + j) * dv), 0);
+                    }
+            }
             __syncthreads();
         };
         for (int c = 0; c < nchunks; c += 2) {
