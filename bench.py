@@ -32,11 +32,13 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0      # dense bf16 MFMA
 METRIC = "tokens/s and achieved TFLOP/s (% roofline), GDN fwd H=16 T=4096 d=128, 1 MI355X"
-KERNEL_SOURCES = ["gated_delta_rule_13_amd/csrc/gdn_pipe.h",
-                  "gated_delta_rule_13_amd/csrc/gdn_recurrent.h",
-                  "gated_delta_rule_13_amd/csrc/gdn_kernels.h",
-                  "gated_delta_rule_13_amd/csrc/gdn_device.h",
-                  "gated_delta_rule_13_amd/csrc/gdn_api.hip"]
+# every source file the kernels are built from: traffic figures taken on
+# other sources are not reported
+KERNEL_SOURCES = sorted(os.path.relpath(os.path.join(dp, f), ROOT)
+                        for dp, _, fs in os.walk(os.path.join(ROOT, "gated_delta_rule_13_amd", "csrc"))
+                        for f in fs if f.endswith((".h", ".hip")))
+
+
 def traffic_file(kernel: str, workload: str) -> str:
     return os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.json")
 
