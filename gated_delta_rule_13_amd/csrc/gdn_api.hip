@@ -27,23 +27,28 @@ bool fast_pair(int C, int dk) {
     return dk == 256 && C <= 32;
 }
 
-// Shapes some kernel covers.  bf16: the fast path's pairs (plus C in
-// {32, 64} with d_k 32 via the generic kernel); f32: C in {16, 32, 64},
-// d_k in {16, 32, 64}.  d_v: multiple of 16 in [16, 1024].
+// Shapes some kernel covers.  bf16: C in {16, 32, 64} with d_k in
+// {32, 64, 96, 128}, d_k 256 with C <= 32 (the fast path; d_k 16 is not
+// built: the bf16 and fp16 MFMAs take 32 elements per k-step, and fp32
+// inputs cover d_k 16); f32: C in {16, 32, 64} with d_k in
+// {16, 32, 64, 128}, d_k 256 with C <= 32 (the generic kernel; C 64 with
+// d_k 256 would need more than the 160 KB of LDS).  d_v: multiple of 16 in
+// [16, 1024].
 bool supported(const gdn_shape& s, std::string* why) {
+    if (s.chunk_size != 16 && s.chunk_size != 32 && s.chunk_size != 64) {
+        *why = "chunk_size must be 16, 32 or 64";
+        return false;
+    }
     if (s.qkv_dtype == GDN_BF16) {
         if (!fast_pair(s.chunk_size, s.d_k)) {
-            *why = "bf16 inputs need chunk_size in {16, 32, 64} and d_k in {32, 64, 96, 128} "
-                   "(d_k 256 with chunk_size <= 32)";
+            *why = "bf16 inputs need d_k in {32, 64, 96, 128}, or 256 with chunk_size <= 32";
             return false;
         }
     } else {
-        if (s.chunk_size != 16 && s.chunk_size != 32 && s.chunk_size != 64) {
-            *why = "f32 inputs need chunk_size 16, 32 or 64";
-            return false;
-        }
-        if (s.d_k != 16 && s.d_k != 32 && s.d_k != 64) {
-            *why = "f32 inputs need d_k in {16, 32, 64}";
+        const bool dk_ok = s.d_k == 16 || s.d_k == 32 || s.d_k == 64 || s.d_k == 128 ||
+                           (s.d_k == 256 && s.chunk_size <= 32);
+        if (!dk_ok) {
+            *why = "f32 inputs need d_k in {16, 32, 64, 128}, or 256 with chunk_size <= 32";
             return false;
         }
     }
@@ -165,7 +170,7 @@ gdn_status run_chunk(const gdn_shape* s, const ChunkArgs& a, Path path, void* st
     gdn::FwdLauncher launch = nullptr;
     int nw = 1;
     bool pipelined = false;
-    if (bf && path == Path::kFast) {
+    if (bf && path == Path::kFast && fast_pair(s->chunk_size, s->d_k)) {
         nw = choose_scan_waves(*s);
         launch = gdn::fast_launcher(s->chunk_size, s->d_k, nw, a.eta != nullptr);
         pipelined = true;
@@ -178,7 +183,7 @@ gdn_status run_chunk(const gdn_shape* s, const ChunkArgs& a, Path path, void* st
         launch = gdn::generic_launcher(s->chunk_size, s->d_k, nw, bf, false);
     }
     if (!launch) return fail(GDN_ERR_UNSUPPORTED, "shape not built for this path");
-    if ((a.dbg_T || a.dbg_V) && !(bf && path == Path::kFast))
+    if ((a.dbg_T || a.dbg_V) && !(bf && path == Path::kFast && fast_pair(s->chunk_size, s->d_k)))
         return fail(GDN_ERR_UNSUPPORTED, "stage outputs exist for the fast bf16 path only");
     gdn::FwdParams p{};
     p.q = a.q;

@@ -1,5 +1,6 @@
 // gdn_inst_generic.hip -- instantiations of the generic fused kernel and of
-// its stage kernel (T, W, U per chunk).
+// its stage kernel (T, W, U per chunk), for bf16 inputs when built with
+// GDN_GEN_BF16=1 and for fp32 inputs when built with GDN_GEN_BF16=0.
 #include "gdn_kernels.h"
 #include "gdn_launch.h"
 
@@ -23,25 +24,36 @@ FwdLauncher pick_nw(int nw, bool prep) {
 }
 }  // namespace
 
-FwdLauncher generic_launcher(int C, int DK, int nw, bool bf16, bool prep) {
-    if (bf16) {
-        if (C == 64 && DK == 128) return pick_nw<64, 128, true>(nw, prep);
-        if (C == 64 && DK == 64) return pick_nw<64, 64, true>(nw, prep);
-        if (C == 64 && DK == 32) return pick_nw<64, 32, true>(nw, prep);
-        if (C == 32 && DK == 128) return pick_nw<32, 128, true>(nw, prep);
-        if (C == 32 && DK == 64) return pick_nw<32, 64, true>(nw, prep);
-        if (C == 32 && DK == 32) return pick_nw<32, 32, true>(nw, prep);
-    } else {
-        if (C == 64 && DK == 64) return pick_nw<64, 64, false>(nw, prep);
-        if (C == 64 && DK == 32) return pick_nw<64, 32, false>(nw, prep);
-        if (C == 64 && DK == 16) return pick_nw<64, 16, false>(nw, prep);
-        if (C == 32 && DK == 64) return pick_nw<32, 64, false>(nw, prep);
-        if (C == 32 && DK == 32) return pick_nw<32, 32, false>(nw, prep);
-        if (C == 32 && DK == 16) return pick_nw<32, 16, false>(nw, prep);
-        if (C == 16 && DK == 64) return pick_nw<16, 64, false>(nw, prep);
-        if (C == 16 && DK == 32) return pick_nw<16, 32, false>(nw, prep);
-        if (C == 16 && DK == 16) return pick_nw<16, 16, false>(nw, prep);
-    }
+#if !defined(GDN_GEN_BF16)
+#error "build with -DGDN_GEN_BF16=1 (bf16 inputs) or -DGDN_GEN_BF16=0 (fp32 inputs)"
+#endif
+#if GDN_GEN_BF16
+FwdLauncher generic_launcher_bf16(int C, int DK, int nw, bool prep) {
+    if (C == 64 && DK == 128) return pick_nw<64, 128, true>(nw, prep);
+    if (C == 64 && DK == 64) return pick_nw<64, 64, true>(nw, prep);
+    if (C == 64 && DK == 32) return pick_nw<64, 32, true>(nw, prep);
+    if (C == 32 && DK == 128) return pick_nw<32, 128, true>(nw, prep);
+    if (C == 32 && DK == 64) return pick_nw<32, 64, true>(nw, prep);
+    if (C == 32 && DK == 32) return pick_nw<32, 32, true>(nw, prep);
     return nullptr;
 }
+#else
+FwdLauncher generic_launcher_f32(int C, int DK, int nw, bool prep) {
+    if (C == 64 && DK == 128) return pick_nw<64, 128, false>(nw, prep);
+    if (C == 64 && DK == 64) return pick_nw<64, 64, false>(nw, prep);
+    if (C == 64 && DK == 32) return pick_nw<64, 32, false>(nw, prep);
+    if (C == 64 && DK == 16) return pick_nw<64, 16, false>(nw, prep);
+    if (C == 32 && DK == 256) return pick_nw<32, 256, false>(nw, prep);
+    if (C == 32 && DK == 128) return pick_nw<32, 128, false>(nw, prep);
+    if (C == 32 && DK == 64) return pick_nw<32, 64, false>(nw, prep);
+    if (C == 32 && DK == 32) return pick_nw<32, 32, false>(nw, prep);
+    if (C == 32 && DK == 16) return pick_nw<32, 16, false>(nw, prep);
+    if (C == 16 && DK == 256) return pick_nw<16, 256, false>(nw, prep);
+    if (C == 16 && DK == 128) return pick_nw<16, 128, false>(nw, prep);
+    if (C == 16 && DK == 64) return pick_nw<16, 64, false>(nw, prep);
+    if (C == 16 && DK == 32) return pick_nw<16, 32, false>(nw, prep);
+    if (C == 16 && DK == 16) return pick_nw<16, 16, false>(nw, prep);
+    return nullptr;
+}
+#endif
 }  // namespace gdn

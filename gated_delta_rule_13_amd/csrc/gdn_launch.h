@@ -41,7 +41,11 @@ FwdLauncher pipe_launcher(int C, int dk, int ns, bool eta);
 
 // generic fused kernel (fp32 inputs, and bf16 shapes the others do not
 // cover) and its stage kernel (T, W, U).
-FwdLauncher generic_launcher(int C, int dk, int nw, bool bf16, bool prep);
+FwdLauncher generic_launcher_bf16(int C, int dk, int nw, bool prep);
+FwdLauncher generic_launcher_f32(int C, int dk, int nw, bool prep);
+inline FwdLauncher generic_launcher(int C, int dk, int nw, bool bf16, bool prep) {
+    return bf16 ? generic_launcher_bf16(C, dk, nw, prep) : generic_launcher_f32(C, dk, nw, prep);
+}
 
 // token-by-token kernel; *rows_per_block receives the state rows one
 // workgroup covers.

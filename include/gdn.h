@@ -62,9 +62,14 @@ typedef struct {
 /*
  * Supported combinations (anything else that is well-formed returns
  * GDN_ERR_UNSUPPORTED):
- *   qkv_dtype GDN_BF16: chunk_size in {16, 32, 64} and d_k in {32, 64, 96,
- *                       128}, or d_k = 256 with chunk_size in {16, 32};
- *   qkv_dtype GDN_F32:  chunk_size in {16, 32, 64}, d_k in {16, 32, 64};
+ *   chunk_size in {16, 32, 64};
+ *   qkv_dtype GDN_BF16: d_k in {32, 64, 96, 128}, or d_k = 256 with
+ *                       chunk_size in {16, 32} (d_k 16 is not built: the bf16
+ *                       and fp16 MFMAs take 32 elements per k-step; fp32
+ *                       inputs cover it);
+ *   qkv_dtype GDN_F32:  d_k in {16, 32, 64, 128}, or d_k = 256 with
+ *                       chunk_size in {16, 32} (chunk 64 at d_k 256 would need
+ *                       more than the 160 KB of LDS of one compute unit);
  *   d_v a multiple of 16 in [16, 1024]; one head's largest tensor (T x
  *   max(d_k, d_v) x 4 bytes) below 2 GiB.
  * T may be any value >= 1; a last chunk shorter than chunk_size is handled
@@ -131,8 +136,9 @@ gdn_status gdn_chunk_fwd_eta(const gdn_shape* s,
  * 16 significant bits), which keeps the normwise error near 1e-5 whatever
  * the gates, at roughly twice the run time of gdn_chunk_fwd.  Shapes: bf16
  * with chunk_size in {32, 64} and d_k in {64, 128} take the pipelined
- * split kernel, other supported bf16 and all f32 shapes the generic one
- * (bf16 chunk_size 16 and d_k 96 / 256 return GDN_ERR_UNSUPPORTED).  eta may
+ * split kernel, bf16 d_k 32 and all f32 shapes the generic one (the other
+ * bf16 shapes, chunk_size 16 or d_k 96 / 256, return GDN_ERR_UNSUPPORTED).
+ * eta may
  * be NULL (eta = beta).  Arguments and conventions as gdn_chunk_fwd_eta,
  * without a workspace.
  */
@@ -154,6 +160,7 @@ gdn_status gdn_chunk_fwd_precise(const gdn_shape* s,
  *          chunk ("从零开始的 GDN 推导", S update), before their rounding to
  *          the fp16 operands of the output and state products.
  * Either may be NULL.  O and S_final are written as by gdn_chunk_fwd_eta.
+ * Shapes: bf16 as for gdn_chunk_fwd; f32 inputs return GDN_ERR_UNSUPPORTED.
  */
 gdn_status gdn_chunk_fwd_stages(const gdn_shape* s,
                                 const void* q, const void* k, const void* v,

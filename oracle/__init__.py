@@ -26,15 +26,15 @@ from .build import build_oracle, library_path
 _LIBS: dict = {}
 
 
-def load(mutant: int = 0, path: str | None = None):
+def load(path: str | None = None):
     """Load (building if needed) the oracle library; cached per path."""
-    path = path or library_path(mutant)
+    path = path or library_path()
     lib = _LIBS.get(path)
     if lib is not None:
         return lib
     if not os.path.exists(path):
-        if path == library_path(mutant):
-            build_oracle(mutant)
+        if path == library_path():
+            build_oracle()
         else:
             raise FileNotFoundError(path)
     lib = ctypes.CDLL(path)
@@ -45,7 +45,6 @@ def load(mutant: int = 0, path: str | None = None):
                                              ctypes.c_int]
     lib.gdn_oracle_recurrent_f64.restype = ctypes.c_int
     lib.gdn_oracle_max_threads.restype = ctypes.c_int
-    lib.gdn_oracle_mutant_id.restype = ctypes.c_int
     _LIBS[path] = lib
     return lib
 

@@ -1,9 +1,11 @@
 """Build the fp64 CPU oracle library (test infrastructure only).
 
 ``build_oracle()`` compiles ``gdn_oracle.c`` with gcc into
-``oracle/libgdn_oracle.so``.  ``build_oracle(mutant=n, out_dir=...)`` builds
-a copy that carries planted mistake ``n``; only the test that checks that the
-oracle's pins catch such mistakes asks for one.
+``oracle/libgdn_oracle.so``.  ``build_oracle(src=..., out=...)`` compiles
+another source file (a copy with a planted mistake, written by the test that
+checks that the oracle's pins catch such mistakes) to another path.
+``sanitize=True`` adds AddressSanitizer and UndefinedBehaviorSanitizer (host
+code only; used by the sanitizer test).
 """
 from __future__ import annotations
 
@@ -14,15 +16,14 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 SRC = os.path.join(HERE, "gdn_oracle.c")
 
 
-def library_path(mutant: int = 0, out_dir: str | None = None) -> str:
-    out_dir = out_dir or HERE
-    name = "libgdn_oracle.so" if mutant == 0 else f"libgdn_oracle_mutant{mutant}.so"
-    return os.path.join(out_dir, name)
+def library_path() -> str:
+    return os.path.join(HERE, "libgdn_oracle.so")
 
 
-def build_oracle(mutant: int = 0, out_dir: str | None = None, quiet: bool = True) -> str:
+def build_oracle(src: str = SRC, out: str | None = None, quiet: bool = True,
+                 sanitize: bool = False) -> str:
     """Compile the oracle; returns the path of the shared library."""
-    out = library_path(mutant, out_dir)
+    out = out or library_path()
     os.makedirs(os.path.dirname(out), exist_ok=True)
     tmp = out + f".tmp{os.getpid()}"
     cmd = [
@@ -30,9 +31,11 @@ def build_oracle(mutant: int = 0, out_dir: str | None = None, quiet: bool = True
         # keep IEEE fp64 semantics: no fast-math, no contraction into FMA
         "-ffp-contract=off",
         "-Wall", "-Wextra",
-        f"-DGDN_ORACLE_MUTANT={int(mutant)}",
-        SRC, "-o", tmp,
     ]
+    if sanitize:
+        cmd += ["-g", "-fno-omit-frame-pointer", "-fsanitize=address,undefined",
+                "-fno-sanitize-recover=undefined"]
+    cmd += [src, "-o", tmp]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError("oracle build failed:\n" + " ".join(cmd) + "\n" + res.stderr)

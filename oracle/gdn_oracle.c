@@ -47,12 +47,6 @@
 #include <omp.h>
 #endif
 
-/* Planted mistakes, compiled in only by the test that checks that the pins
- * catch them (GDN_ORACLE_MUTANT = 1..N).  Default build: 0, none. */
-#ifndef GDN_ORACLE_MUTANT
-#define GDN_ORACLE_MUTANT 0
-#endif
-
 static void run_one_sequence(int64_t T, int64_t dk, int64_t dv,
                              const double* q, const double* k, const double* v,
                              const double* alpha, const double* beta,
@@ -70,22 +64,6 @@ static void run_one_sequence(int64_t T, int64_t dk, int64_t dv,
         double a = alpha ? alpha[t] : 1.0;
         double b = beta[t];
         double e = eta ? eta[t] : beta[t];
-#if GDN_ORACLE_MUTANT == 6
-        /* gate index shifted by one token */
-        a = alpha ? (t > 0 ? alpha[t - 1] : 1.0) : 1.0;
-#endif
-#if GDN_ORACLE_MUTANT == 7
-        /* write strength forced to one */
-        e = 1.0;
-#endif
-#if GDN_ORACLE_MUTANT == 3
-        /* exclusive output: read out the state before token t is absorbed */
-        for (int64_t i = 0; i < dv; ++i) {
-            double acc = 0.0;
-            for (int64_t j = 0; j < dk; ++j) acc += S[i * dk + j] * qt[j];
-            O[t * dv + i] = acc;
-        }
-#endif
         /* u = S k_t */
         for (int64_t i = 0; i < dv; ++i) {
             double acc = 0.0;
@@ -96,24 +74,9 @@ static void run_one_sequence(int64_t T, int64_t dk, int64_t dv,
         for (int64_t i = 0; i < dv; ++i) {
             for (int64_t j = 0; j < dk; ++j) {
                 double s = S[i * dk + j];
-#if GDN_ORACLE_MUTANT == 1
-                /* gate dropped from the erased state, applied to the write */
-                S[i * dk + j] = (s - b * u[i] * kt[j]) + a * e * vt[i] * kt[j];
-#elif GDN_ORACLE_MUTANT == 2
-                /* sign of the erase term flipped */
-                S[i * dk + j] = a * (s + b * u[i] * kt[j]) + e * vt[i] * kt[j];
-#elif GDN_ORACLE_MUTANT == 4
-                /* write outer product transposed (only differs for d_k == d_v) */
-                S[i * dk + j] = a * (s - b * u[i] * kt[j]) + e * vt[j % dv] * kt[i % dk];
-#elif GDN_ORACLE_MUTANT == 5
-                /* gate applied to the write as well */
-                S[i * dk + j] = a * (s - b * u[i] * kt[j] + e * vt[i] * kt[j]);
-#else
                 S[i * dk + j] = a * (s - b * u[i] * kt[j]) + e * vt[i] * kt[j];
-#endif
             }
         }
-#if GDN_ORACLE_MUTANT != 3
         /* o_t = S q_t (state after token t) */
         double* ot = O + t * dv;
         for (int64_t i = 0; i < dv; ++i) {
@@ -121,7 +84,6 @@ static void run_one_sequence(int64_t T, int64_t dk, int64_t dv,
             for (int64_t j = 0; j < dk; ++j) acc += S[i * dk + j] * qt[j];
             ot[i] = acc;
         }
-#endif
     }
 }
 
@@ -174,6 +136,3 @@ int gdn_oracle_max_threads(void)
     return 1;
 #endif
 }
-
-/* Which planted mistake this build carries (0 = none). */
-int gdn_oracle_mutant_id(void) { return GDN_ORACLE_MUTANT; }

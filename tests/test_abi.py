@@ -17,7 +17,13 @@ HEADER = os.path.join(ROOT, "include", "gdn.h")
 
 @pytest.fixture(scope="module")
 def lib():
-    if not os.path.exists(_lib.LIB_PATH):
+    # the sanitizer test runs this file against an instrumented build of the
+    # same sources, named by GDN_TEST_LIB
+    override = os.environ.get("GDN_TEST_LIB")
+    if override:
+        _lib.LIB_PATH = override
+        _lib._lib = None
+    elif not os.path.exists(_lib.LIB_PATH):
         from gated_delta_rule_13_amd.build import build
         build()
     return _lib.load()
@@ -62,8 +68,10 @@ def fwd(lib, s, **ptrs):
 @pytest.mark.parametrize("kw,expected", [
     (dict(B=0), 2), (dict(H=-1), 2), (dict(T=0), 2), (dict(d_k=0), 2),
     (dict(qkv_dtype=7), 3), (dict(o_dtype=-1), 3),
-    (dict(chunk_size=48), 4), (dict(d_k=256), 4), (dict(d_k=16), 4), (dict(d_k=48), 4),
-    (dict(d_v=40), 4), (dict(d_v=2048), 4), (dict(qkv_dtype=1, d_k=128), 4),
+    (dict(chunk_size=48), 4), (dict(d_k=256), 4), (dict(d_k=16), 4), (dict(d_k=8), 4),
+    (dict(d_k=48), 4),
+    (dict(d_v=40), 4), (dict(d_v=2048), 4), (dict(qkv_dtype=1, d_k=256), 4),
+    (dict(qkv_dtype=1, d_k=96), 4), (dict(d_k=16, chunk_size=8), 4),
     (dict(T=5_000_000), 4),
 ])
 def test_bad_shapes_rejected(lib, kw, expected):
@@ -117,9 +125,11 @@ def test_new_entries_validate(lib):
                                     None, None, None) == 4
 
 
+
 def test_workspace_query_and_strings(lib):
     for kw in (dict(), dict(qkv_dtype=1, d_k=16, d_v=16, chunk_size=16),
-               dict(chunk_size=32), dict(d_v=256), dict(chunk_size=16), dict(d_k=96, d_v=192)):
+               dict(chunk_size=32), dict(d_v=256), dict(chunk_size=16), dict(d_k=96, d_v=192),
+               dict(qkv_dtype=1, d_k=128), dict(qkv_dtype=1, d_k=256, chunk_size=32)):
         assert lib.gdn_chunk_fwd_workspace_bytes(ctypes.byref(shape(**kw))) == 0
     for code in range(7):
         assert lib.gdn_status_string(code).decode()
