@@ -95,15 +95,42 @@ int choose_waves(const gdn_shape& s) {
     return best;
 }
 
-// Scan waves per workgroup of the pipelined kernels (16 value columns each):
-// the largest of 4, 2 that divides d_v / 16 and still gives one workgroup per
-// compute unit (256), else 1.
+// Compute units of the current device (256 on MI355X), read once.
+int device_cus() {
+    static const int n = [] {
+        int dev = 0, cus = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            cus <= 0)
+            return 256;
+        return cus;
+    }();
+    return n;
+}
+
+// Scan waves per workgroup of the pipelined kernels (16 value columns each,
+// one workgroup per compute unit): the choice of 1, 2 or 4 (dividing
+// d_v / 16) that needs the fewest rounds of workgroups over the compute
+// units, a four-wave workgroup weighing 1.4 rounds (its prep waves serve
+// four slices; measured at d_k 96, d_v 192: 160 us for one round of them
+// against about 110 us per round of two-wave workgroups); ties go to the
+// smaller workgroup.
 int choose_scan_waves(const gdn_shape& s) {
     const long heads = (long)s.B * s.H;
     const int cols16 = s.d_v / 16;
-    for (int ns : {4, 2})
-        if (cols16 % ns == 0 && heads * (cols16 / ns) >= 256) return ns;
-    return 1;
+    const long cus = device_cus();
+    int best = 1;
+    double best_cost = 1e300;
+    for (int ns : {1, 2, 4}) {
+        if (cols16 % ns != 0) continue;
+        const long wgs = heads * (cols16 / ns);
+        const double cost = (double)((wgs + cus - 1) / cus) * (ns == 4 ? 1.4 : 1.0);
+        if (cost < best_cost) {
+            best = ns;
+            best_cost = cost;
+        }
+    }
+    return best;
 }
 
 bool pipe_shape(const gdn_shape& s) {

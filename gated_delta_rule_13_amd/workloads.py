@@ -4,7 +4,7 @@ This module holds input generation only -- none of the method's arithmetic --
 so that the GPU path and the CPU oracle can both be fed from it without
 sharing any code with each other.
 
-Six workloads, named by what they are.  All draws come from one CPU
+Seven workloads, named by what they are.  All draws come from one CPU
 ``torch.Generator`` seeded with ``seed``, in the fixed order
 q, k, v, S0, beta source, alpha source, reflection mask; each is drawn in
 float32 with the full shape.  q and k are L2-normalised per row in float32
@@ -22,6 +22,8 @@ many_short     64, 8, 512, 128, 128, 32                    bf16    beta ~ U(0,1)
                                                                    are reflections: beta = 2 / (k^T k), alpha = 1; S0 = 0
 decode         64, 16, 1, 128, 128, -                      bf16    beta = sigmoid(N), alpha = exp(-softplus(N) * 0.05),
                                                                    S0 = 0.02 N: one decode step of the recurrent form
+olmo_hybrid    2, 30, 4096, 96, 192, 64                    bf16    beta = 2 sigmoid(N) (erase strength in (0, 2)),
+                                                                   alpha = exp(-softplus(N) * 0.05), S0 = 0
 =============  ==========================================  ======  ============================
 
 v ~ N(0, 1) everywhere.  Alpha of exactly one is passed as ``None`` (the
@@ -48,7 +50,7 @@ class Workload:
     dv: int
     chunk: int
     dtype: str                 # "bf16" or "f32": dtype of q, k, v
-    beta_kind: str = "sigmoid"  # "sigmoid" | "uniform"
+    beta_kind: str = "sigmoid"  # "sigmoid" | "sigmoid2" (2 sigmoid) | "uniform"
     alpha_kind: str = "softplus"  # "softplus" | "one" | "uniform"
     alpha_scale: float = 0.0   # s in exp(-softplus(N) * s)
     s0_std: float = 0.0        # 0 => S0 = None
@@ -75,6 +77,10 @@ WORKLOADS = {
     # chunk field is unused there)
     "decode": Workload("decode", 64, 16, 1, 128, 128, 64, "bf16", alpha_scale=0.05,
                        s0_std=0.02),
+    # the head shape of the Olmo Hybrid models' gated delta rule layers (30
+    # heads, q/k dimension 96, v dimension 192, erase strength 2 beta)
+    "olmo_hybrid": Workload("olmo_hybrid", 2, 30, 4096, 96, 192, 64, "bf16",
+                            beta_kind="sigmoid2", alpha_scale=0.05),
 }
 
 _TORCH_DTYPE = {"bf16": torch.bfloat16, "f32": torch.float32}
@@ -99,6 +105,8 @@ def make_inputs(w: Workload, seed: int = 0) -> dict:
         S0 = w.s0_std * torch.randn(B, H, dv, dk, generator=g)
     if w.beta_kind == "sigmoid":
         beta = torch.sigmoid(torch.randn(B, H, T, generator=g))
+    elif w.beta_kind == "sigmoid2":
+        beta = 2.0 * torch.sigmoid(torch.randn(B, H, T, generator=g))
     elif w.beta_kind == "uniform":
         beta = torch.rand(B, H, T, generator=g)
     else:

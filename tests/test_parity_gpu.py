@@ -73,6 +73,17 @@ def test_workload_many_short_full_size():
     check(x, O, S)
 
 
+def test_workload_olmo_hybrid_full_size():
+    """"从电路复杂性理论的角度分析大模型的可并行性和表达能力--Olmo Hybrid 系列",
+    Olmo Hybrid architecture: 30 heads, q/k dimension 96, v dimension 192,
+    erase strength 2 beta.  B * H = 60 is not a multiple of 8 (no XCD
+    grouping of a head's workgroups)."""
+    x = make_inputs(WORKLOADS["olmo_hybrid"])
+    say("case: olmo_hybrid B2 H30 T4096 dk96 dv192 C64 bf16, beta in (0, 2) (all 60 heads)")
+    O, S = run_gpu(x, 64)
+    check(x, O, S)
+
+
 # ---------------------------------------------------- shapes, tiles, tails
 
 BF16_SHAPES = [
