@@ -611,6 +611,20 @@ __global__ __launch_bounds__((NS + fast_prep_waves(NS)) * 64) void gdn_fwd_fast_
         auto pair_op = [&](const f32x4* tiles, int sidx) __attribute__((always_inline)) {
             return cat_h(to_h4(tiles[2 * sidx]), 2 * sidx + 1 < NT ? to_h4(tiles[2 * sidx + 1]) : zero_h4());
         };
+        // first k-step of the next chunk's key and query operands, read at
+        // the end of the previous chunk (those tiles are staged two chunks
+        // ahead) so that phase A starts on its products
+        h8 kf0[NT], qf0[NT];
+        auto kq_first = [&](int cc) __attribute__((always_inline)) {
+            lds_h* kl = lds_opaque(&s.K[cc % 3][n][8 * h]);
+            lds_h* ql = lds_opaque(&s.Q[cc & 1][n][8 * h]);
+#pragma unroll
+            for (int rt = 0; rt < NT; ++rt) {
+                kf0[rt] = lds_at<h8>(kl, 16 * rt * L::KP);
+                qf0[rt] = lds_at<h8>(ql, 16 * rt * L::KP);
+            }
+        };
+        kq_first(0);
         // one chunk; PAR = parity of c (the LDS buffer of Q, T and P; keys by c mod 3)
         auto chunk = [&](auto PAR, int c) __attribute__((always_inline)) {
             constexpr int buf = decltype(PAR)::value;
@@ -630,8 +644,8 @@ __global__ __launch_bounds__((NS + fast_prep_waves(NS)) * 64) void gdn_fwd_fast_
                 h8 kf[NT], qf[NT];
 #pragma unroll
                 for (int rt = 0; rt < NT; ++rt) {
-                    kf[rt] = lds_at<h8>(kl, 16 * rt * L::KP + 32 * ss);
-                    qf[rt] = lds_at<h8>(ql, 16 * rt * L::KP + 32 * ss);
+                    kf[rt] = ss == 0 ? kf0[rt] : lds_at<h8>(kl, 16 * rt * L::KP + 32 * ss);
+                    qf[rt] = ss == 0 ? qf0[rt] : lds_at<h8>(ql, 16 * rt * L::KP + 32 * ss);
                 }
 #pragma unroll
                 for (int rt = 0; rt < NT; ++rt) X[rt] = mfma_h(kf[rt], sh[ss], X[rt]);
@@ -754,6 +768,7 @@ __global__ __launch_bounds__((NS + fast_prep_waves(NS)) * 64) void gdn_fwd_fast_
                     Sacc[t] = mfma_h(ktop[t], vd[ss], Sacc[t]);
                     if (ss + 1 < NTS) ktop[t] = kt_one(ss + 1, t);
                 }
+            if (c + 1 < nchunks) kq_first(c + 1);
             // O^T = diag(exp g) Z^T + V'^T P^T  (lane: row 16 rt + n, columns 4h..4h+3):
             // all products first, then the stores under one branch on the
             // output type; output rows past the end of the sequence fall
