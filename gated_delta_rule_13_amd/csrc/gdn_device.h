@@ -54,15 +54,21 @@ __device__ __forceinline__ uint4 buf_load_16B(buf_t r, uint32_t off) {
     const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
     return make_uint4(v[0], v[1], v[2], v[3]);
 }
-// Streaming output stores (written once, never read back by the kernel):
-// non-temporal (cache-policy bit 2 of the gfx950 buffer store).  Writing the
-// 16-byte pieces through at system scope as well (bits 1 and 16) measured
-// the same on the main shape and 6 % slower on d_v = 256 with the
-// fp16-operand kernel; 8-byte pieces written through would reach memory as
-// partial sectors.
+// Streaming output stores (written once, never read back by the kernel).
+// Cache-policy bits of the gfx950 buffer store: 1 = sc0, 2 = nt, 16 = sc1.
+// buf_store: non-temporal only.  buf_store_wt: 16-byte pieces written
+// through at system scope as well, which leaves no partly written lines for
+// a later write-back (measured: the written bytes equal the output size,
+// against 16 % more with non-temporal only; the same speed up to d_v = 192,
+// 6 % slower at d_v = 256).  8-byte pieces written through would reach
+// memory as partial sectors, so bf16 output stays non-temporal only.
+constexpr int kStoreNtSys = 1 | 2 | 16;
 constexpr int kStoreNt = 2;
 __device__ __forceinline__ void buf_store(buf_t r, uint32_t off, f32x4 v) {
     __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, (int)off, 0, kStoreNt);
+}
+__device__ __forceinline__ void buf_store_wt(buf_t r, uint32_t off, f32x4 v) {
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, (int)off, 0, kStoreNtSys);
 }
 __device__ __forceinline__ void buf_store(buf_t r, uint32_t off, bf16x4 v) {
     __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, v), r, (int)off, 0, kStoreNt);

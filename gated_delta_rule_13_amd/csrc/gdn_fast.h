@@ -236,6 +236,9 @@ __global__ __launch_bounds__((NS + fast_prep_waves(NS)) * 64) void gdn_fwd_fast_
         tile = blockIdx.x % p.n_tiles;
         bh = blockIdx.x / p.n_tiles;
     }
+    // padding workgroups of an XCD-grouped grid (B * H rounded up to a
+    // multiple of 8) have no head: they leave before any barrier
+    if (bh >= p.B * p.H) return;
     const int T = p.T, dv = p.dv;
     const int nchunks = (T + C - 1) / C;
     const __bf16* kb = reinterpret_cast<const __bf16*>(p.k) + (size_t)bh * T * DK;
@@ -788,6 +791,9 @@ __global__ __launch_bounds__((NS + fast_prep_waves(NS)) * 64) void gdn_fwd_fast_
 #pragma unroll
                 for (int rt = 0; rt < NT; ++rt)
                     buf_store(obuf, (row0 + 16u * rt * dv) * 2, __builtin_convertvector(o[rt], bf16x4));
+            } else if (p.o_wt) {
+#pragma unroll
+                for (int rt = 0; rt < NT; ++rt) buf_store_wt(obuf, (row0 + 16u * rt * dv) * 4, o[rt]);
             } else {
 #pragma unroll
                 for (int rt = 0; rt < NT; ++rt) buf_store(obuf, (row0 + 16u * rt * dv) * 4, o[rt]);

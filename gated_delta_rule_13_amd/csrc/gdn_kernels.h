@@ -43,6 +43,8 @@ struct FwdParams {
     int n_tiles;          // value-column tiles per head
     int o_bf16;           // O stored as bf16 (else fp32)
     int xcd_groups;       // pipelined kernel: place a head's tiles on one XCD
+                          // (the grid then covers B * H rounded up to a multiple of 8)
+    int o_wt;             // fp32 output written through (else non-temporal only)
     const float* eta;     // write strength; may be null: eta = beta
     float* dbg_T;         // fast kernel, stage output: T per chunk [B,H,NT,C,C] (may be null)
     float* dbg_V;         // fast kernel, stage output: pseudo-values V' [B,H,T,d_v] (may be null)

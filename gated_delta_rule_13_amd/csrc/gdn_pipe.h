@@ -256,6 +256,9 @@ __global__ __launch_bounds__((NS + kPrepWaves) * 64) void gdn_fwd_pipe_kernel(Fw
         tile = blockIdx.x % p.n_tiles;
         bh = blockIdx.x / p.n_tiles;
     }
+    // padding workgroups of an XCD-grouped grid (B * H rounded up to a
+    // multiple of 8) have no head: they leave before any barrier
+    if (bh >= p.B * p.H) return;
     const int T = p.T, dv = p.dv;
     const int nchunks = (T + C - 1) / C;
     const __bf16* kb = reinterpret_cast<const __bf16*>(p.k) + (size_t)bh * T * DK;
@@ -835,6 +838,13 @@ __global__ __launch_bounds__((NS + kPrepWaves) * 64) void gdn_fwd_pipe_kernel(Fw
                     const f32x4 o = s.eg[buf][r] * Zt[rt] + PVt[rt];
                     buf_store(obuf, (uint32_t)((t0 + r) * dv + col0 + 4 * h) * 2,
                               __builtin_convertvector(o, bf16x4));
+                }
+            } else if (p.o_wt) {
+#pragma unroll
+                for (int rt = 0; rt < NT; ++rt) {
+                    const int r = 16 * rt + n;
+                    const f32x4 o = s.eg[buf][r] * Zt[rt] + PVt[rt];
+                    buf_store_wt(obuf, (uint32_t)((t0 + r) * dv + col0 + 4 * h) * 4, o);
                 }
             } else {
 #pragma unroll
