@@ -77,6 +77,23 @@ def cpu_model() -> str:
     return platform.processor() or "unknown"
 
 
+def segments_in_workspace(w, ws_bytes: int, o_bf16: bool) -> int:
+    """Segments per sequence of a chunked call, from its workspace size (the
+    layout of include/gdn.h: end states and transitions, carried queries,
+    then zero-state outputs for bf16 O; 0 bytes: the plain form)."""
+    if not ws_bytes:
+        return 1
+    up = lambda n: (n + 255) // 256 * 256
+    bh = w.B * w.H
+    rest = bh * w.T * w.dk * 4
+    if o_bf16:
+        rest = up(rest) + bh * w.T * w.dv * 4
+    for nseg in range(2, w.T + 1):
+        if up(bh * nseg * (w.dv + w.dk) * w.dk * 4) + rest == ws_bytes:
+            return nseg
+    raise RuntimeError("workspace size matches no segment count")
+
+
 def cpu_baseline(x, w, target_seconds=10.0):
     """Time the fp64 oracle on this host over a bounded sample of the same
     workload: whole (b, h) sequences (all of them when the workload is small
@@ -125,11 +142,14 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain device copy of known size (for counter scaling)")
+    ap.add_argument("--seg-chunks", type=int, default=0,
+                    help="chunks per segment of the sequence-parallel form (gdn_chunk_fwd_seq); "
+                         "0: the choice gdn_chunk_fwd makes, a large value: the plain form")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: this build runs on one GPU only (every (b,h) sequence is independent; "
-              "multi-GPU sharding is described in DESIGN.md but not built)", file=sys.stderr)
+        print("bench.py: runs on one GPU only (every (b,h) sequence is independent; "
+              "sharding heads over GPUs is not implemented)", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -169,21 +189,29 @@ def main():
         gdn.gdn_recurrent_fwd(d["q"], d["k"], d["v"], d["alpha"], d["beta"], S,
                               o_dtype=o_dtype, O=O, S_final=S)
     else:
-        gdn.gdn_chunk_fwd(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["S0"],
-                          chunk_size=w.chunk, o_dtype=o_dtype, O=O, S_final=S)
+        gdn.gdn_chunk_fwd_seq(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["S0"],
+                              chunk_size=w.chunk, seg_chunks=args.seg_chunks, o_dtype=o_dtype,
+                              O=O, S_final=S)
     lib = _lib.load()
     ptr = lambda t: None if t is None else ctypes.c_void_p(t.data_ptr())
     shape = gdn.make_shape(w.B, w.H, w.T, w.dk, w.dv, w.chunk, d["q"].dtype, o_dtype)
     sp = ctypes.byref(shape)
     hstream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    # workspace of the sequence-parallel form (none for the plain form)
+    ws_bytes = 0 if recurrent else lib.gdn_chunk_fwd_seq_workspace_bytes(sp, args.seg_chunks)
+    ws = torch.empty(ws_bytes + 256, dtype=torch.uint8, device=dev) if ws_bytes else None
+    ws_ptr = None if ws is None else ctypes.c_void_p((ws.data_ptr() + 255) // 256 * 256)
     if recurrent:
         cargs = (sp, ptr(d["q"]), ptr(d["k"]), ptr(d["v"]), ptr(d["alpha"]), ptr(d["beta"]),
                  ptr(S), ptr(O), ptr(S), hstream)
         entry = lib.gdn_recurrent_fwd
     else:
         cargs = (sp, ptr(d["q"]), ptr(d["k"]), ptr(d["v"]), ptr(d["alpha"]), ptr(d["beta"]),
-                 ptr(d["S0"]), ptr(O), ptr(S), None, 0, hstream)
+                 ptr(d["S0"]), ptr(O), ptr(S), ws_ptr, ws_bytes, hstream)
         entry = lib.gdn_chunk_fwd
+        if args.seg_chunks:
+            cargs = (sp, args.seg_chunks) + cargs[1:6] + (None,) + cargs[6:]
+            entry = lib.gdn_chunk_fwd_seq
 
     def step():
         st = entry(*cargs)
@@ -228,7 +256,8 @@ def main():
     value = tokens / (wall / args.steps)
     achieved_gbs = alg_bytes / mean_kern_s / 1e9
     kernel = "gdn_recurrent" if recurrent else "gdn_fwd"
-    traffic = measured_traffic(kernel, w.name) if args.o_dtype == "f32" else None
+    traffic = (measured_traffic(kernel, w.name)
+               if args.o_dtype == "f32" and not args.seg_chunks else None)
 
     rec = {
         "metric": METRIC,
@@ -246,6 +275,8 @@ def main():
         "config": {"workload": w.name, "B": w.B, "H": w.H, "T": w.T, "d_k": w.dk, "d_v": w.dv,
                    "chunk": None if recurrent else w.chunk, "o_dtype": args.o_dtype,
                    "path": "recurrent" if recurrent else "chunked",
+                   "segments": None if recurrent else
+                   segments_in_workspace(w, ws_bytes, o_dtype != torch.float32),
                    "parallelism": "none (1 GPU)"},
         "head_tokens_per_s": tokens * w.H / (wall / args.steps),
         "tflops": alg_flops / (wall / args.steps) / 1e12,

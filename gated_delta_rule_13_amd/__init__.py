@@ -16,6 +16,7 @@ import ctypes
 from ._lib import (EXPORTS, GDN_BF16, GDN_F32, GdnError, GdnShape, check, load)
 
 __all__ = ["gdn_chunk_fwd", "gdn_chunk_fwd_eta", "gdn_chunk_fwd_precise", "gdn_chunk_fwd_stages",
+           "gdn_chunk_fwd_seq", "gdn_chunk_fwd_seq_workspace_bytes",
            "gdn_chunk_prep", "gdn_chunk_fwd_workspace_bytes",
            "gdn_recurrent_fwd", "gdn_recurrent_fwd_eta",
            "gdn_status_string", "gdn_last_error", "gdn_version", "GdnError", "GdnShape",
@@ -73,6 +74,27 @@ def gdn_chunk_fwd_workspace_bytes(shape: GdnShape) -> int:
     return int(n)
 
 
+def gdn_chunk_fwd_seq_workspace_bytes(shape: GdnShape, seg_chunks: int) -> int:
+    n = load().gdn_chunk_fwd_seq_workspace_bytes(ctypes.byref(shape), int(seg_chunks))
+    if n == ctypes.c_size_t(-1).value:
+        raise GdnError(4, load().gdn_last_error().decode())
+    return int(n)
+
+
+def _workspace(nbytes, dev):
+    """Device workspace of nbytes (256-byte aligned), or None."""
+    if not nbytes:
+        return None
+    torch = _torch()
+    return torch.empty(nbytes + 256, dtype=torch.uint8, device=dev)
+
+
+def _ws_ptr(ws) -> int | None:
+    if ws is None:
+        return None
+    return (ws.data_ptr() + 255) // 256 * 256
+
+
 def _chunk_call(entry, q, k, v, alpha, beta, S0, chunk_size, o_dtype, O, S_final, stream, eta,
                 extra=()):
     torch = _torch()
@@ -100,15 +122,26 @@ def _chunk_call(entry, q, k, v, alpha, beta, S0, chunk_size, o_dtype, O, S_final
     hs = _stream_handle(dev, stream)
     if entry == "fast":
         ws_bytes = gdn_chunk_fwd_workspace_bytes(shape)
-        ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None
+        ws = _workspace(ws_bytes, dev)
         if eta is None:
             st = lib.gdn_chunk_fwd(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha),
-                                   _ptr(beta), _ptr(S0), _ptr(O), _ptr(S_final), _ptr(ws),
+                                   _ptr(beta), _ptr(S0), _ptr(O), _ptr(S_final), _ws_ptr(ws),
                                    ws_bytes, hs)
         else:
             st = lib.gdn_chunk_fwd_eta(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v),
                                        _ptr(alpha), _ptr(beta), _ptr(eta), _ptr(S0), _ptr(O),
-                                       _ptr(S_final), _ptr(ws), ws_bytes, hs)
+                                       _ptr(S_final), _ws_ptr(ws), ws_bytes, hs)
+    elif entry == "seq":
+        seg_chunks, ws = extra
+        ws_bytes = gdn_chunk_fwd_seq_workspace_bytes(shape, seg_chunks)
+        if ws is None:
+            ws = _workspace(ws_bytes, dev)
+        elif ws.numel() < ws_bytes + 256 or ws.dtype != torch.uint8 or ws.device != dev:
+            raise ValueError(f"workspace must be a uint8 tensor of at least {ws_bytes + 256} "
+                             f"bytes on {dev}")
+        st = lib.gdn_chunk_fwd_seq(ctypes.byref(shape), int(seg_chunks), _ptr(q), _ptr(k),
+                                   _ptr(v), _ptr(alpha), _ptr(beta), _ptr(eta), _ptr(S0),
+                                   _ptr(O), _ptr(S_final), _ws_ptr(ws), ws_bytes, hs)
     elif entry == "precise":
         st = lib.gdn_chunk_fwd_precise(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v),
                                        _ptr(alpha), _ptr(beta), _ptr(eta), _ptr(S0), _ptr(O),
@@ -134,6 +167,19 @@ def gdn_chunk_fwd(q, k, v, alpha, beta, S0=None, chunk_size: int = 64, o_dtype=N
     operand kernel (gdn_chunk_fwd_precise is the split-bf16 alternative)."""
     return _chunk_call("fast", q, k, v, alpha, beta, S0, chunk_size, o_dtype, O, S_final,
                        stream, eta)
+
+
+def gdn_chunk_fwd_seq(q, k, v, alpha, beta, S0=None, chunk_size: int = 64, seg_chunks: int = 0,
+                      o_dtype=None, O=None, S_final=None, stream=None, eta=None, workspace=None):
+    """gdn_chunk_fwd with the sequence-parallel form chosen by the caller:
+    segments of seg_chunks chunks run at once, then a combine over segments
+    and a correction of the later segments' outputs (0: the choice
+    gdn_chunk_fwd makes).  workspace: None (allocated here) or a uint8 cuda
+    tensor of at least gdn_chunk_fwd_seq_workspace_bytes + 256 bytes; its
+    contents after the call are laid out as include/gdn.h states (the data
+    starts at the first 256-byte aligned address of the tensor)."""
+    return _chunk_call("seq", q, k, v, alpha, beta, S0, chunk_size, o_dtype, O, S_final,
+                       stream, eta, extra=(seg_chunks, workspace))
 
 
 def gdn_chunk_fwd_precise(q, k, v, alpha, beta, S0=None, chunk_size: int = 64, o_dtype=None,

@@ -48,7 +48,8 @@ def units() -> list[tuple[str, str, list[str]]]:
            ("gdn_inst_pipe.o", "gdn_inst_pipe.hip", []),
            ("gdn_inst_generic_bf16.o", "gdn_inst_generic.hip", ["-DGDN_GEN_BF16=1"]),
            ("gdn_inst_generic_f32.o", "gdn_inst_generic.hip", ["-DGDN_GEN_BF16=0"]),
-           ("gdn_inst_rec.o", "gdn_inst_rec.hip", [])]
+           ("gdn_inst_rec.o", "gdn_inst_rec.hip", []),
+           ("gdn_inst_seq.o", "gdn_inst_seq.hip", [])]
     for c, d in FAST_PAIRS:
         out.append((f"gdn_inst_fast_c{c}_d{d}.o", "gdn_inst_fast.hip", [f"-DGDN_C={c}", f"-DGDN_DK={d}"]))
     return out

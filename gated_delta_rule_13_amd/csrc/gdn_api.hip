@@ -133,6 +133,108 @@ int choose_scan_waves(const gdn_shape& s) {
     return best;
 }
 
+// ---------------------------------------------------------------------------
+// Sequence-parallel form of the default path.  When the heads and value
+// tiles of a call leave compute units idle, each sequence is cut into
+// segments of whole chunks that run at once (the later ones from a zero
+// state, with d_k extra transition rows), then one more launch combines the
+// segments and corrects the later segments' outputs (gdn_seq.h).
+// Cost model in microseconds, fitted to measurements on MI355X (one fused
+// kernel iteration: 1.4 us at d_k <= 64, 1.6 us above, times 1.25 for two
+// scan waves and 1.75 for four):
+//   plain  rounds(B H d_v / (16 ns)) (n_chunks + 2) it
+//   seq    rounds(B H (n_v + (n_seg - 1) (n_v + n_k))) (L + 2) it
+//          + 6.5 (the second launch and its first memory round trip)
+//          + (n_seg - 1) step   (the combine's dependent steps: 1 us at
+//                                d_k <= 64, 2.5 us at 96 / 128, 4 us at 256)
+//          + the correction's bytes at 1.5 TB/s
+// with rounds(x) = ceil(x / CUs), n_v and n_k the value and transition
+// tiles per segment and L the chunks per segment.  The sequence-parallel
+// form is taken when it is estimated at least 10 % faster.
+struct Plan {
+    int ns = 1;           // scan waves per workgroup
+    int nseg = 1;         // segments per sequence
+    int seg_len = 0;      // tokens per segment
+    size_t off_q = 0, off_o = 0, bytes = 0;   // workspace layout
+};
+
+double iter_us(int dk, int ns) {
+    return (dk <= 64 ? 1.4 : 1.6) * (ns == 1 ? 1.0 : ns == 2 ? 1.25 : 1.75);
+}
+long rounds_over_cus(long wgs) {
+    const long cus = device_cus();
+    return (wgs + cus - 1) / cus;
+}
+
+double plain_cost(const gdn_shape& s, int ns) {
+    const long nchunks = (s.T + s.chunk_size - 1) / s.chunk_size;
+    const long wgs = (long)s.B * s.H * (s.d_v / (16 * ns));
+    return (double)rounds_over_cus(wgs) * (double)(nchunks + 2) * iter_us(s.d_k, ns);
+}
+
+double seq_cost(const gdn_shape& s, int ns, int seg_chunks) {
+    const long nchunks = (s.T + s.chunk_size - 1) / s.chunk_size;
+    const long nseg = (nchunks + seg_chunks - 1) / seg_chunks;
+    const long nv = s.d_v / (16 * ns), nk = s.d_k / (16 * ns);
+    const long bh = (long)s.B * s.H;
+    const long wgs = bh * (nv + (nseg - 1) * (nv + nk));
+    const double fused = (double)rounds_over_cus(wgs) * (double)(seg_chunks + 2) * iter_us(s.d_k, ns);
+    const double step = s.d_k <= 64 ? 1.0 : s.d_k <= 128 ? 2.5 : 4.0;
+    const double corr_tokens = (double)bh * (double)(s.T - (long)seg_chunks * s.chunk_size);
+    const double corr_bytes = corr_tokens * 4.0 * (s.d_k + 2.0 * s.d_v);
+    return fused + 6.5 + step * (double)(nseg - 1) + corr_bytes / 1.5e6;
+}
+
+void plan_workspace(const gdn_shape& s, Plan* pl) {
+    pl->off_q = pl->off_o = pl->bytes = 0;
+    if (pl->nseg <= 1) return;
+    auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+    const size_t bh = (size_t)s.B * s.H;
+    pl->off_q = up(bh * pl->nseg * (size_t)(s.d_v + s.d_k) * s.d_k * 4);
+    pl->off_o = up(pl->off_q + bh * (size_t)s.T * s.d_k * 4);
+    pl->bytes = pl->off_o + (s.o_dtype == GDN_BF16 ? bh * (size_t)s.T * s.d_v * 4 : 0);
+}
+
+// Plan of a default-path call with bf16 inputs on the fused kernel:
+// seg_chunks 0 picks by the cost model, seg_chunks > 0 fixes the chunks per
+// segment (one segment: the plain form).  The segmented form runs one scan
+// wave per workgroup (the most workgroups, the shortest iteration); the
+// model is only trusted where its fused pass is one round of workgroups
+// over the compute units and there are at most 8 segments, so the default
+// plan stays inside that range.
+Plan make_plan(const gdn_shape& s, int seg_chunks) {
+    Plan pl;
+    pl.ns = choose_scan_waves(s);
+    pl.seg_len = s.T;
+    const long nchunks = (s.T + s.chunk_size - 1) / s.chunk_size;
+    int best_L = 0;
+    if (seg_chunks > 0) {
+        if (seg_chunks < nchunks) best_L = seg_chunks;
+    } else {
+        const long bh = (long)s.B * s.H;
+        const long nv = s.d_v / 16, nk = s.d_k / 16;
+        double best = 0.9 * plain_cost(s, pl.ns);
+        for (long L = 1; L < nchunks; ++L) {
+            const long nseg = (nchunks + L - 1) / L;
+            // only the smallest L of each segment count
+            if (L > 1 && nseg == (nchunks + L - 2) / (L - 1)) continue;
+            if (nseg > 8 || rounds_over_cus(bh * (nv + (nseg - 1) * (nv + nk))) > 1) continue;
+            const double c = seq_cost(s, 1, (int)L);
+            if (c < best) {
+                best = c;
+                best_L = (int)L;
+            }
+        }
+    }
+    if (best_L > 0) {
+        pl.ns = 1;
+        pl.seg_len = best_L * s.chunk_size;
+        pl.nseg = (int)((nchunks + best_L - 1) / best_L);
+    }
+    plan_workspace(s, &pl);
+    return pl;
+}
+
 bool pipe_shape(const gdn_shape& s) {
     return s.qkv_dtype == GDN_BF16 && (s.chunk_size == 32 || s.chunk_size == 64) &&
            (s.d_k == 64 || s.d_k == 128);
@@ -182,7 +284,10 @@ struct ChunkArgs {
     float* dbg_V;
 };
 
-gdn_status run_chunk(const gdn_shape* s, const ChunkArgs& a, Path path, void* stream) {
+// seg_chunks: < 0 the plain form only; 0 the default plan; > 0 that many
+// chunks per segment (default path, fused kernel).
+gdn_status run_chunk(const gdn_shape* s, const ChunkArgs& a, Path path, void* stream,
+                     int seg_chunks = -1, void* workspace = nullptr, size_t workspace_bytes = 0) {
     g_last_error.clear();
     gdn_status st = validate_shape(s);
     if (st != GDN_OK) return st;
@@ -194,11 +299,24 @@ gdn_status run_chunk(const gdn_shape* s, const ChunkArgs& a, Path path, void* st
         (a.dbg_T && !aligned16(a.dbg_T)) || (a.dbg_V && !aligned16(a.dbg_V)))
         return fail(GDN_ERR_UNSUPPORTED, "tensor pointers must be 16-byte aligned");
     const bool bf = s->qkv_dtype == GDN_BF16;
+    const bool fused = bf && path == Path::kFast && fast_pair(s->chunk_size, s->d_k);
+    Plan plan;
+    plan.ns = choose_scan_waves(*s);
+    if (fused && seg_chunks >= 0) plan = make_plan(*s, seg_chunks);
+    if (seg_chunks > 0 && !fused &&
+        (long)seg_chunks * s->chunk_size < (long)s->T)
+        return fail(GDN_ERR_UNSUPPORTED, "segments exist on the default path with bf16 inputs only");
+    if (plan.nseg > 1) {
+        if (!workspace || workspace_bytes < plan.bytes)
+            return fail(GDN_ERR_WORKSPACE, "workspace smaller than gdn_chunk_fwd_workspace_bytes");
+        if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+            return fail(GDN_ERR_UNSUPPORTED, "workspace must be 256-byte aligned");
+    }
     gdn::FwdLauncher launch = nullptr;
     int nw = 1;
     bool pipelined = false;
-    if (bf && path == Path::kFast && fast_pair(s->chunk_size, s->d_k)) {
-        nw = choose_scan_waves(*s);
+    if (fused) {
+        nw = plan.ns;
         launch = gdn::fast_launcher(s->chunk_size, s->d_k, nw, a.eta != nullptr);
         pipelined = true;
     } else if (bf && pipe_shape(*s)) {
@@ -228,21 +346,62 @@ gdn_status run_chunk(const gdn_shape* s, const ChunkArgs& a, Path path, void* st
     p.H = s->H;
     p.T = s->T;
     p.dv = s->d_v;
-    p.n_tiles = s->d_v / (16 * nw);
+    p.n_tiles_v = s->d_v / (16 * nw);
+    p.n_tiles = p.n_tiles_v;
     p.o_bf16 = s->o_dtype == GDN_BF16;
-    // The workgroups of one head are placed on one XCD (ids congruent mod 8,
-    // sharing that XCD's L2 copy of the head's keys and queries); with B * H
-    // not a multiple of 8 the grid is padded and the extra workgroups exit.
-    const long heads = (long)s->B * s->H;
+    p.nseg = 1;
+    p.seg_len = s->T;
+    gdn::SeqLauncher finish = nullptr;
+    if (plan.nseg > 1) {
+        finish = gdn::seq_launcher(s->d_k);
+        if (!finish) return fail(GDN_ERR_UNSUPPORTED, "segments not built for this d_k");
+        char* ws = static_cast<char*>(workspace);
+        p.nseg = plan.nseg;
+        p.seg_len = plan.seg_len;
+        p.n_tiles = p.n_tiles_v + s->d_k / (16 * nw);
+        p.seg_state = reinterpret_cast<float*>(ws);
+        p.seg_q = reinterpret_cast<float*>(ws + plan.off_q);
+        p.seg_o = p.o_bf16 ? reinterpret_cast<float*>(ws + plan.off_o) : nullptr;
+    }
+    // The workgroups of one unit (head and segment) are placed on one XCD
+    // (ids congruent mod 8, sharing that XCD's L2 copy of the unit's keys and
+    // queries); with units not a multiple of 8 the grid is padded and the
+    // extra workgroups exit.
+    const long units = (long)s->B * s->H * p.nseg;
     p.xcd_groups = pipelined;
-    const long grid_heads = pipelined ? (heads + 7) / 8 * 8 : heads;
+    const long grid_units = pipelined ? (units + 7) / 8 * 8 : units;
     // fp32 output written through at system scope keeps the written bytes at
     // the output size; at d_v >= 256 plain non-temporal stores measured 6 %
     // faster (the write-back of partly written lines costs bytes, not time)
     p.o_wt = s->d_v < 256;
-    const long nblocks = grid_heads * p.n_tiles;
+    const long nblocks = grid_units * p.n_tiles;
     if (nblocks > 0x7fffffffL) return fail(GDN_ERR_BAD_SHAPE, "grid too large");
-    launch(p, nblocks, reinterpret_cast<hipStream_t>(stream));
+    if (finish) {
+        // the finishing kernel: (head, later segment, token group) units padded
+        // to a multiple of 8, d_v / 16 row blocks each
+        const long units = (long)s->B * s->H * (p.nseg - 1) *
+                           ((p.seg_len + gdn::seq_group_tokens(s->d_k) - 1) /
+                            gdn::seq_group_tokens(s->d_k));
+        if ((units + 7) / 8 * 8 * (s->d_v / 16) > 0x7fffffffL)
+            return fail(GDN_ERR_BAD_SHAPE, "grid too large");
+    }
+    const hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+    launch(p, nblocks, hs);
+    if (finish) {
+        gdn::SeqParams q{};
+        q.BH = s->B * s->H;
+        q.nseg = p.nseg;
+        q.seg_len = p.seg_len;
+        q.T = s->T;
+        q.dv = s->d_v;
+        q.seg_state = p.seg_state;
+        q.seg_q = p.seg_q;
+        q.seg_o = p.seg_o;
+        q.O = a.O;
+        q.o_bf16 = p.o_bf16;
+        q.S_final = a.S_final;
+        finish(q, hs);
+    }
     return check_launch();
 }
 
@@ -251,8 +410,29 @@ gdn_status run_chunk(const gdn_shape* s, const ChunkArgs& a, Path path, void* st
 extern "C" {
 
 size_t gdn_chunk_fwd_workspace_bytes(const gdn_shape* s) {
+    return gdn_chunk_fwd_seq_workspace_bytes(s, 0);
+}
+
+size_t gdn_chunk_fwd_seq_workspace_bytes(const gdn_shape* s, int seg_chunks) {
     if (validate_shape(s) != GDN_OK) return (size_t)-1;
-    return 0;
+    if (seg_chunks < 0) {
+        g_last_error = "seg_chunks must be >= 0";
+        return (size_t)-1;
+    }
+    if (s->qkv_dtype != GDN_BF16) return 0;
+    return make_plan(*s, seg_chunks).bytes;
+}
+
+gdn_status gdn_chunk_fwd_seq(const gdn_shape* s, int seg_chunks, const void* q, const void* k,
+                             const void* v, const float* alpha, const float* beta,
+                             const float* eta, const float* S0, void* O, float* S_final,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+    if (seg_chunks < 0) {
+        g_last_error = "seg_chunks must be >= 0";
+        return GDN_ERR_BAD_SHAPE;
+    }
+    return run_chunk(s, ChunkArgs{q, k, v, alpha, beta, eta, S0, O, S_final, nullptr, nullptr},
+                     Path::kFast, stream, seg_chunks, workspace, workspace_bytes);
 }
 
 gdn_status gdn_chunk_fwd(const gdn_shape* s, const void* q, const void* k, const void* v,
@@ -266,10 +446,8 @@ gdn_status gdn_chunk_fwd_eta(const gdn_shape* s, const void* q, const void* k, c
                              const float* alpha, const float* beta, const float* eta,
                              const float* S0, void* O, float* S_final, void* workspace,
                              size_t workspace_bytes, void* stream) {
-    (void)workspace;
-    (void)workspace_bytes;
     return run_chunk(s, ChunkArgs{q, k, v, alpha, beta, eta, S0, O, S_final, nullptr, nullptr},
-                     Path::kFast, stream);
+                     Path::kFast, stream, 0, workspace, workspace_bytes);
 }
 
 gdn_status gdn_chunk_fwd_precise(const gdn_shape* s, const void* q, const void* k, const void* v,

@@ -227,29 +227,39 @@ __global__ __launch_bounds__((NS + fast_prep_waves(NS)) * 64) void gdn_fwd_fast_
     // staging lane 0..64*NSTG-1 on the stager waves
     const int plane = (pw >= 0 ? R::stager(pw) : 0) * 64 + lane;
 
-    int tile, bh;
+    // unit = (head, segment); the tiles of one unit share its keys and queries
+    int tile, unit;
     if (p.xcd_groups) {
         const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
         tile = slot % p.n_tiles;
-        bh = xcd + 8 * (slot / p.n_tiles);
+        unit = xcd + 8 * (slot / p.n_tiles);
     } else {
         tile = blockIdx.x % p.n_tiles;
-        bh = blockIdx.x / p.n_tiles;
+        unit = blockIdx.x / p.n_tiles;
     }
-    // padding workgroups of an XCD-grouped grid (B * H rounded up to a
-    // multiple of 8) have no head: they leave before any barrier
-    if (bh >= p.B * p.H) return;
-    const int T = p.T, dv = p.dv;
+    const int nseg = p.nseg;
+    // padding workgroups of an XCD-grouped grid (units rounded up to a
+    // multiple of 8) have none: they leave before any barrier, and so do the
+    // transition tiles of a first segment (it starts from the true state)
+    if (unit >= p.B * p.H * nseg) return;
+    const int bh = unit / nseg, seg = unit - bh * nseg;
+    const bool trans = tile >= p.n_tiles_v;
+    if (trans && seg == 0) return;
+    // this segment's tokens: T from token tbase of the sequence
+    const int tbase = seg * p.seg_len;
+    const int T = min(p.T - tbase, p.seg_len), dv = p.dv;
+    const size_t tok0 = (size_t)bh * p.T + tbase;
     const int nchunks = (T + C - 1) / C;
-    const __bf16* kb = reinterpret_cast<const __bf16*>(p.k) + (size_t)bh * T * DK;
-    const __bf16* qb = reinterpret_cast<const __bf16*>(p.q) + (size_t)bh * T * DK;
-    const __bf16* vb = reinterpret_cast<const __bf16*>(p.v) + (size_t)bh * T * dv;
-    const float* ab = p.alpha ? p.alpha + (size_t)bh * T : nullptr;
-    const float* bb = p.beta + (size_t)bh * T;
-    const float* eb = p.eta ? p.eta + (size_t)bh * T : nullptr;
+    const __bf16* kb = reinterpret_cast<const __bf16*>(p.k) + tok0 * DK;
+    const __bf16* qb = reinterpret_cast<const __bf16*>(p.q) + tok0 * DK;
+    const __bf16* vb = reinterpret_cast<const __bf16*>(p.v) + tok0 * dv;
+    const float* ab = p.alpha ? p.alpha + tok0 : nullptr;
+    const float* bb = p.beta + tok0;
+    const float* eb = p.eta ? p.eta + tok0 : nullptr;
     const buf_t kbuf = buffer_over(kb, (uint32_t)T * DK * 2);
     const buf_t qbuf = buffer_over(qb, (uint32_t)T * DK * 2);
-    const int col0 = tile * DVT + 16 * wave;   // scan waves: first value column
+    // scan waves: first value column (transition tiles: first transition row)
+    const int col0 = (trans ? tile - p.n_tiles_v : tile) * DVT + 16 * wave;
 
     auto mod3 = [](int x) { return (x + 3) % 3; };   // x >= -3
 
@@ -581,7 +591,8 @@ __global__ __launch_bounds__((NS + fast_prep_waves(NS)) * 64) void gdn_fwd_fast_
         // lane (n, h) holds V[16 rt + n][col0 + 8 (h & 1) .. + 7] (lanes h >= 2
         // repeat lanes h - 2; the selector gives them weight zero)
         uint4 vraw[NT];
-        const buf_t vbuf = buffer_over(vb, (uint32_t)T * dv * 2);
+        // (transition tiles: zero values, an empty buffer reads zero)
+        const buf_t vbuf = buffer_over(vb, trans ? 0u : (uint32_t)T * dv * 2);
         const uint32_t voff = 2u * (n * dv + col0 + 8 * (h & 1));
         auto v_load = [&](int cc) __attribute__((always_inline)) {
             const uint32_t t0 = (uint32_t)cc * C;
@@ -593,14 +604,39 @@ __global__ __launch_bounds__((NS + fast_prep_waves(NS)) * 64) void gdn_fwd_fast_
 #pragma unroll
         for (int e = 0; e < 8; ++e) vsel[e] = (__bf16)((h < 2 && 8 * h + e == n) ? 1.f : 0.f);
 
-        const int osz = p.o_bf16 ? 2 : 4;
-        const buf_t obuf = buffer_over(reinterpret_cast<const char*>(p.O) + (size_t)bh * T * dv * osz,
-                                       (uint32_t)T * dv * osz);
+        // outputs: O (fp32 or bf16, row stride d_v); for a later segment with
+        // bf16 O, fp32 partial outputs into seg_o; for transition tiles the
+        // transformed queries into seg_q (fp32, row stride d_k)
+        const void* obase;
+        int ostr = dv;
+        bool obf = false;
+        if (trans) {
+            obase = p.seg_q + tok0 * DK;
+            ostr = DK;
+        } else if (seg > 0 && p.seg_o) {
+            obase = p.seg_o + tok0 * dv;
+        } else {
+            obf = p.o_bf16;
+            obase = reinterpret_cast<const char*>(p.O) + tok0 * dv * (obf ? 2 : 4);
+        }
+        const buf_t obuf = buffer_over(obase, (uint32_t)T * ostr * (obf ? 2 : 4));
+        // initial state: S0 rows (first segment), zero (later segments) or
+        // identity rows (transition tiles); end state: S_final, or this
+        // segment's rows of seg_state (transition rows stored transposed,
+        // element (row, k) at k * d_k + row)
         const size_t sb = (size_t)bh * dv * DK + (size_t)(col0 + n) * DK;
+        const float* s0p = (seg == 0 && p.S0) ? p.S0 + sb : nullptr;
+        const size_t seg_base = ((size_t)bh * nseg + seg) * (dv + DK) * DK;
+        float* sfp = nseg == 1 ? p.S_final + sb
+                     : trans   ? p.seg_state + seg_base + (size_t)dv * DK + col0 + n
+                               : p.seg_state + seg_base + (size_t)(col0 + n) * DK;
+        const int sst = trans ? DK : 1;
 #pragma unroll
         for (int t = 0; t < NK; ++t)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) Sacc[t][j] = p.S0 ? p.S0[sb + 16 * t + 4 * h + j] : 0.f;
+            for (int j = 0; j < 4; ++j)
+                Sacc[t][j] = trans ? (col0 + n == 16 * t + 4 * h + j ? 1.f : 0.f)
+                                   : s0p ? s0p[16 * t + 4 * h + j] : 0.f;
         v_load(0);
         // wait here for the initial state (and the first values): at the loop
         // head the state registers must not look like pending loads, or every
@@ -786,17 +822,17 @@ __global__ __launch_bounds__((NS + fast_prep_waves(NS)) * 64) void gdn_fwd_fast_
                 });
                 o[rt] = egr[rt] * Zt[rt] + acc;
             });
-            const uint32_t row0 = (uint32_t)(t0 + n) * dv + col0 + 4 * h;
-            if (p.o_bf16) {
+            const uint32_t row0 = (uint32_t)(t0 + n) * ostr + col0 + 4 * h;
+            if (obf) {
 #pragma unroll
                 for (int rt = 0; rt < NT; ++rt)
-                    buf_store(obuf, (row0 + 16u * rt * dv) * 2, __builtin_convertvector(o[rt], bf16x4));
+                    buf_store(obuf, (row0 + 16u * rt * ostr) * 2, __builtin_convertvector(o[rt], bf16x4));
             } else if (p.o_wt) {
 #pragma unroll
-                for (int rt = 0; rt < NT; ++rt) buf_store_wt(obuf, (row0 + 16u * rt * dv) * 4, o[rt]);
+                for (int rt = 0; rt < NT; ++rt) buf_store_wt(obuf, (row0 + 16u * rt * ostr) * 4, o[rt]);
             } else {
 #pragma unroll
-                for (int rt = 0; rt < NT; ++rt) buf_store(obuf, (row0 + 16u * rt * dv) * 4, o[rt]);
+                for (int rt = 0; rt < NT; ++rt) buf_store(obuf, (row0 + 16u * rt * ostr) * 4, o[rt]);
             }
             if (p.dbg_V) {
                 // stage output: V' rows of this chunk (rows past the end of the
@@ -823,7 +859,7 @@ __global__ __launch_bounds__((NS + fast_prep_waves(NS)) * 64) void gdn_fwd_fast_
 #pragma unroll
         for (int t = 0; t < NK; ++t)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) p.S_final[sb + 16 * t + 4 * h + j] = Sacc[t][j];
+            for (int j = 0; j < 4; ++j) sfp[(16 * t + 4 * h + j) * sst] = Sacc[t][j];
     }
 }
 

@@ -48,6 +48,22 @@ struct FwdParams {
     const float* eta;     // write strength; may be null: eta = beta
     float* dbg_T;         // fast kernel, stage output: T per chunk [B,H,NT,C,C] (may be null)
     float* dbg_V;         // fast kernel, stage output: pseudo-values V' [B,H,T,d_v] (may be null)
+    // Sequence-parallel launch of the fast kernel (nseg > 1).  Each sequence
+    // is cut into nseg segments of seg_len tokens (a multiple of the chunk
+    // size), all run at once.  The first segment starts from S0 and its
+    // outputs are final; every later one starts from a zero state, and its
+    // tiles from n_tiles_v on carry the d_k rows of the segment's transition
+    // (identity state, zero values), whose outputs are the segment's queries
+    // carried through its transitions.
+    int nseg;             // segments per sequence (1: the whole sequence)
+    int seg_len;          // tokens per segment
+    int n_tiles_v;        // value-column tiles (tiles past them: transition rows)
+    float* seg_state;     // [B*H][nseg][d_v + d_k][d_k]: each segment's end state (the first
+                          // from S0, the others from zero), then its transition M
+                          // transposed (d_k x d_k, element (r, k) of M at k * d_k + r)
+    float* seg_q;         // [B*H*T][d_k]: transformed queries of the later segments
+    float* seg_o;         // [B*H*T][d_v]: fp32 outputs of the later segments from a zero
+                          // state when O is bf16 (null: they are written to O)
 };
 
 // LDS layout of one workgroup.  Rows are padded by 16 bytes.

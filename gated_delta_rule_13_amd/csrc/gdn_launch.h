@@ -7,11 +7,13 @@
 
 #include "gdn_kernels.h"
 #include "gdn_recurrent.h"
+#include "gdn_seq.h"
 
 namespace gdn {
 
 using FwdLauncher = void (*)(const FwdParams&, long nblocks, hipStream_t);
 using RecLauncher = void (*)(const RecParams&, long nblocks, hipStream_t);
+using SeqLauncher = void (*)(const SeqParams&, hipStream_t);
 
 // fp16-operand fused kernel (bf16 inputs): C in {16, 32, 64}, d_k in
 // {32, 64, 96, 128} (and 256 with C <= 32), ns scan waves in {1, 2, 4}.
@@ -46,6 +48,11 @@ FwdLauncher generic_launcher_f32(int C, int dk, int nw, bool prep);
 inline FwdLauncher generic_launcher(int C, int dk, int nw, bool bf16, bool prep) {
     return bf16 ? generic_launcher_bf16(C, dk, nw, prep) : generic_launcher_f32(C, dk, nw, prep);
 }
+
+// finishing kernel of a sequence-parallel run of the fused kernel (the
+// combine over segments and the correction of the later segments'
+// outputs): d_k in {32, 64, 96, 128, 256}.
+SeqLauncher seq_launcher(int dk);
 
 // token-by-token kernel; *rows_per_block receives the state rows one
 // workgroup covers.

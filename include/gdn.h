@@ -86,9 +86,12 @@ typedef struct {
  */
 
 /*
- * Bytes of device workspace gdn_chunk_fwd needs for this shape (0 for the
- * fused kernels of this version).  Returns (size_t)-1 if the shape is
- * invalid or unsupported.
+ * Bytes of device workspace gdn_chunk_fwd (and gdn_chunk_fwd_eta) needs for
+ * this shape on the current device: 0 unless the call takes the
+ * sequence-parallel form (see gdn_chunk_fwd_seq), which it does for bf16
+ * inputs when the heads and value tiles would leave compute units idle (few
+ * heads, long sequences).  Returns (size_t)-1 if the shape is invalid or
+ * unsupported.
  */
 size_t gdn_chunk_fwd_workspace_bytes(const gdn_shape* s);
 
@@ -124,6 +127,45 @@ gdn_status gdn_chunk_fwd(const gdn_shape* s,
  * Everything else as gdn_chunk_fwd.
  */
 gdn_status gdn_chunk_fwd_eta(const gdn_shape* s,
+                             const void* q, const void* k, const void* v,
+                             const float* alpha, const float* beta, const float* eta,
+                             const float* S0, void* O, float* S_final,
+                             void* workspace, size_t workspace_bytes,
+                             void* stream);
+
+/*
+ * gdn_chunk_fwd_eta with the sequence-parallel form chosen by the caller.
+ * The state recurrence is linear in the state, so it is associative and can
+ * be evaluated by a parallel scan ("Параллельность RNN?", section
+ * "Уровень 2"); the chunk form already passes each chunk's end state to the
+ * next ("从零开始的 GDN 推导", 总结).  Each sequence is cut into segments of
+ * seg_chunks chunks (the last one shorter).  All segments run at once: the
+ * first from S0; every later one from a zero state, together with the d_k
+ * rows of its transition M = A_first ... A_last (A_t = alpha_t (I - beta_t
+ * k_t k_t^T)) started from the identity, whose outputs are the queries
+ * carried through the segment, qm_t = A_first ... A_t q_t.  A combine over
+ * segments (X_{j+1} = X_j M_j + E_j, E_j the end state from zero) and a
+ * correction o_t += X_j qm_t finish the pass.  Results equal those of the
+ * plain form up to rounding (the combine and the correction multiply
+ * split-bf16 operands, about 16 significant bits, with fp32 accumulation).
+ *   seg_chunks  0: the form and segment length gdn_chunk_fwd would choose;
+ *               >= 1: segments of that many chunks (one segment, i.e.
+ *               seg_chunks >= ceil(T / chunk_size), is the plain form);
+ *               < 0: GDN_ERR_BAD_SHAPE.  More than one segment needs bf16
+ *               inputs (else GDN_ERR_UNSUPPORTED).
+ * workspace: at least gdn_chunk_fwd_seq_workspace_bytes(s, seg_chunks)
+ * bytes of device memory, 256-byte aligned (GDN_ERR_WORKSPACE if smaller or
+ * NULL when needed).  After the call it holds, from offset 0,
+ *   [B*H][n_seg][d_v + d_k][d_k] float: rows 0..d_v-1 of segment j: its end
+ *     state from a zero state (segment 0: from S0); rows d_v.. : M_j
+ *     transposed, row c holding M_j[0..d_k-1][c] (segments >= 1);
+ *   then, at the next multiple of 256 bytes, [B*H*T][d_k] float: qm_t for
+ *     the tokens of segments >= 1;
+ *   then (bf16 O only) [B*H*T][d_v] float: outputs from a zero state.
+ * Everything else as gdn_chunk_fwd_eta.
+ */
+size_t gdn_chunk_fwd_seq_workspace_bytes(const gdn_shape* s, int seg_chunks);
+gdn_status gdn_chunk_fwd_seq(const gdn_shape* s, int seg_chunks,
                              const void* q, const void* k, const void* v,
                              const float* alpha, const float* beta, const float* eta,
                              const float* S0, void* O, float* S_final,

@@ -176,3 +176,56 @@ def test_recurrent_null_and_misaligned_rejected(lib):
         assert rec(lib, shape(), **{name: None}) == 1, name
     for name in ("q", "k", "v", "beta", "O", "S", "alpha", "S0"):
         assert rec(lib, shape(), **{name: ctypes.c_void_p(0x10004)}) == 4, name
+
+
+def seq(lib, s, seg_chunks, ws=None, ws_bytes=0, **ptrs):
+    p = dict(q=FAKE, k=FAKE, v=FAKE, alpha=None, beta=FAKE, eta=None, S0=None, O=FAKE, S=FAKE)
+    p.update(ptrs)
+    return lib.gdn_chunk_fwd_seq(ctypes.byref(s), seg_chunks, p["q"], p["k"], p["v"], p["alpha"],
+                                 p["beta"], p["eta"], p["S0"], p["O"], p["S"], ws, ws_bytes, None)
+
+
+def test_seq_entry_validates(lib):
+    """gdn_chunk_fwd_seq rejects before any launch: a negative segment
+    length, segments of fp32 inputs, a missing, short or misaligned
+    workspace."""
+    big = ctypes.c_size_t(-1).value
+    s = shape(T=300)
+    assert seq(lib, s, -1) == 2
+    assert lib.gdn_chunk_fwd_seq_workspace_bytes(ctypes.byref(s), -1) == big
+    assert seq(lib, shape(qkv_dtype=1, T=300), 1) == 4
+    need = lib.gdn_chunk_fwd_seq_workspace_bytes(ctypes.byref(s), 1)
+    assert need > 0
+    assert seq(lib, s, 1) == 5
+    assert seq(lib, s, 1, ctypes.c_void_p(0x100000), need - 1) == 5
+    assert seq(lib, s, 1, ctypes.c_void_p(0x100010), need) == 4
+
+
+def test_seq_workspace_layout(lib):
+    """Workspace bytes of a forced segmentation follow the layout that
+    include/gdn.h states: end states and transitions, carried queries, and
+    (bf16 O) zero-state outputs, each region 256-byte aligned."""
+    up = lambda n: (n + 255) // 256 * 256
+    B, H, T, dk, dv, C, L = 2, 3, 300, 64, 96, 32, 2
+    nseg = -(-T // (L * C))
+    for o_dtype in (1, 0):
+        s = shape(B=B, H=H, T=T, d_k=dk, d_v=dv, chunk_size=C, o_dtype=o_dtype)
+        want = up(B * H * nseg * (dv + dk) * dk * 4) + B * H * T * dk * 4
+        if o_dtype == 0:
+            want = up(want) + B * H * T * dv * 4
+        assert lib.gdn_chunk_fwd_seq_workspace_bytes(ctypes.byref(s), L) == want
+    # one segment (or fp32 inputs): the plain form, no workspace
+    s = shape(T=T)
+    assert lib.gdn_chunk_fwd_seq_workspace_bytes(ctypes.byref(s), 5) == 0
+    assert lib.gdn_chunk_fwd_seq_workspace_bytes(ctypes.byref(shape(qkv_dtype=1, T=T)), 1) == 0
+
+
+def test_default_plan_host_logic(lib):
+    """The default plan (a 256-CU device when none is present): segments for
+    one head over 4096 tokens, none for the main shape or short sequences."""
+    ws = lambda **kw: lib.gdn_chunk_fwd_workspace_bytes(ctypes.byref(shape(**kw)))
+    assert ws(B=1, H=1, T=4096) > 0
+    assert ws(B=2, H=4, T=1024, d_k=64, d_v=64) > 0
+    assert ws(B=4, H=16, T=4096) == 0
+    assert ws(B=1, H=32, T=32768, d_v=256) == 0
+    assert ws(B=1, H=1, T=64) == 0
