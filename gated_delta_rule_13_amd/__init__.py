@@ -16,7 +16,7 @@ import ctypes
 from ._lib import (EXPORTS, GDN_BF16, GDN_F32, GdnError, GdnShape, check, load)
 
 __all__ = ["gdn_chunk_fwd", "gdn_chunk_fwd_eta", "gdn_chunk_fwd_precise", "gdn_chunk_fwd_stages",
-           "gdn_chunk_fwd_seq", "gdn_chunk_fwd_seq_workspace_bytes",
+           "gdn_chunk_fwd_seq", "gdn_chunk_fwd_seq_workspace_bytes", "gdn_chunk_fwd_seq_noalloc",
            "gdn_chunk_prep", "gdn_chunk_fwd_workspace_bytes",
            "gdn_recurrent_fwd", "gdn_recurrent_fwd_eta",
            "gdn_status_string", "gdn_last_error", "gdn_version", "GdnError", "GdnShape",
@@ -142,6 +142,11 @@ def _chunk_call(entry, q, k, v, alpha, beta, S0, chunk_size, o_dtype, O, S_final
         st = lib.gdn_chunk_fwd_seq(ctypes.byref(shape), int(seg_chunks), _ptr(q), _ptr(k),
                                    _ptr(v), _ptr(alpha), _ptr(beta), _ptr(eta), _ptr(S0),
                                    _ptr(O), _ptr(S_final), _ws_ptr(ws), ws_bytes, hs)
+    elif entry == "noalloc":
+        (seg_chunks,) = extra
+        st = lib.gdn_chunk_fwd_seq_noalloc(ctypes.byref(shape), int(seg_chunks), _ptr(q), _ptr(k),
+                                           _ptr(v), _ptr(alpha), _ptr(beta), _ptr(eta), _ptr(S0),
+                                           _ptr(O), _ptr(S_final), hs)
     elif entry == "precise":
         st = lib.gdn_chunk_fwd_precise(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v),
                                        _ptr(alpha), _ptr(beta), _ptr(eta), _ptr(S0), _ptr(O),
@@ -180,6 +185,16 @@ def gdn_chunk_fwd_seq(q, k, v, alpha, beta, S0=None, chunk_size: int = 64, seg_c
     starts at the first 256-byte aligned address of the tensor)."""
     return _chunk_call("seq", q, k, v, alpha, beta, S0, chunk_size, o_dtype, O, S_final,
                        stream, eta, extra=(seg_chunks, workspace))
+
+
+def gdn_chunk_fwd_seq_noalloc(q, k, v, alpha, beta, S0=None, chunk_size: int = 64,
+                              seg_chunks: int = 0, o_dtype=None, O=None, S_final=None,
+                              stream=None, eta=None):
+    """gdn_chunk_fwd_seq with the library's own 64 MiB scratch instead of a
+    workspace (the C entry allocates nothing; pass O and S_final to keep the
+    whole call free of allocation).  Calls that overlap on one GPU race."""
+    return _chunk_call("noalloc", q, k, v, alpha, beta, S0, chunk_size, o_dtype, O, S_final,
+                       stream, eta, extra=(seg_chunks,))
 
 
 def gdn_chunk_fwd_precise(q, k, v, alpha, beta, S0=None, chunk_size: int = 64, o_dtype=None,

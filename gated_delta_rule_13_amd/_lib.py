@@ -22,7 +22,7 @@ STATUS = {
 
 # Every symbol include/gdn.h declares.
 EXPORTS = ("gdn_chunk_fwd_workspace_bytes", "gdn_chunk_fwd", "gdn_chunk_fwd_eta",
-           "gdn_chunk_fwd_seq_workspace_bytes", "gdn_chunk_fwd_seq",
+           "gdn_chunk_fwd_seq_workspace_bytes", "gdn_chunk_fwd_seq", "gdn_chunk_fwd_seq_noalloc",
            "gdn_chunk_fwd_precise", "gdn_chunk_fwd_stages",
            "gdn_chunk_prep", "gdn_recurrent_fwd", "gdn_recurrent_fwd_eta",
            "gdn_status_string", "gdn_last_error", "gdn_version")
@@ -68,6 +68,9 @@ def load():
     lib.gdn_chunk_fwd_seq.argtypes = [sp, ctypes.c_int, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                       ctypes.c_size_t, vp]
     lib.gdn_chunk_fwd_seq.restype = ctypes.c_int
+    lib.gdn_chunk_fwd_seq_noalloc.argtypes = [sp, ctypes.c_int, vp, vp, vp, vp, vp, vp, vp, vp,
+                                              vp, vp]
+    lib.gdn_chunk_fwd_seq_noalloc.restype = ctypes.c_int
     lib.gdn_chunk_fwd_precise.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.gdn_chunk_fwd_precise.restype = ctypes.c_int
     lib.gdn_chunk_fwd_stages.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]

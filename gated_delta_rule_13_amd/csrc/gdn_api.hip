@@ -4,6 +4,7 @@
 
 #include <cstdint>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "gdn.h"
@@ -407,6 +408,43 @@ gdn_status run_chunk(const gdn_shape* s, const ChunkArgs& a, Path path, void* st
 
 }  // namespace
 
+namespace {
+
+// Scratch of gdn_chunk_fwd_seq_noalloc (for callers that cannot allocate):
+// a file-scope device array, one copy per GPU, held until the process ends.
+// Host code never uses the array's name as an address: its device address
+// is looked up once per device with hipGetSymbolAddress (with that device
+// current) and kept in scratch_addr.
+constexpr size_t kScratchBytes = (size_t)64 << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_addr[kMaxDevices] = {};
+
+// Device address of the current device's scratch array, or null (error
+// recorded) when it cannot be found.
+void* scratch_addr() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+        g_last_error = "no current HIP device (or device index beyond 63)";
+        return nullptr;
+    }
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_addr[dev]) {
+        void* ptr = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !ptr) {
+            g_last_error = std::string("hipGetSymbolAddress(scratch): ") + hipGetErrorString(e);
+            return nullptr;
+        }
+        g_scratch_addr[dev] = ptr;
+    }
+    return g_scratch_addr[dev];
+}
+
+}  // namespace
+
 extern "C" {
 
 size_t gdn_chunk_fwd_workspace_bytes(const gdn_shape* s) {
@@ -433,6 +471,34 @@ gdn_status gdn_chunk_fwd_seq(const gdn_shape* s, int seg_chunks, const void* q, 
     }
     return run_chunk(s, ChunkArgs{q, k, v, alpha, beta, eta, S0, O, S_final, nullptr, nullptr},
                      Path::kFast, stream, seg_chunks, workspace, workspace_bytes);
+}
+
+gdn_status gdn_chunk_fwd_seq_noalloc(const gdn_shape* s, int seg_chunks, const void* q,
+                                     const void* k, const void* v, const float* alpha,
+                                     const float* beta, const float* eta, const float* S0,
+                                     void* O, float* S_final, void* stream) {
+    g_last_error.clear();
+    if (seg_chunks < 0) {
+        g_last_error = "seg_chunks must be >= 0";
+        return GDN_ERR_BAD_SHAPE;
+    }
+    const size_t need = gdn_chunk_fwd_seq_workspace_bytes(s, seg_chunks);
+    if (need == (size_t)-1) {
+        const gdn_status st = validate_shape(s);
+        return st != GDN_OK ? st : GDN_ERR_BAD_SHAPE;
+    }
+    if (need > kScratchBytes)
+        return fail(GDN_ERR_WORKSPACE,
+                    "this plan needs " + std::to_string(need) +
+                        " bytes of scratch, more than the library's 64 MiB (67108864 bytes); "
+                        "use gdn_chunk_fwd_seq with a workspace");
+    void* ws = nullptr;
+    if (need > 0) {
+        ws = scratch_addr();
+        if (!ws) return GDN_ERR_HIP;
+    }
+    return run_chunk(s, ChunkArgs{q, k, v, alpha, beta, eta, S0, O, S_final, nullptr, nullptr},
+                     Path::kFast, stream, seg_chunks, ws, need > 0 ? kScratchBytes : 0);
 }
 
 gdn_status gdn_chunk_fwd(const gdn_shape* s, const void* q, const void* k, const void* v,

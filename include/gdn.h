@@ -173,6 +173,26 @@ gdn_status gdn_chunk_fwd_seq(const gdn_shape* s, int seg_chunks,
                              void* stream);
 
 /*
+ * gdn_chunk_fwd_seq without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation): the workspace is a 64 MiB
+ * (67108864-byte) device array inside the library, one copy per GPU,
+ * looked up on the first call on each device and held until the process
+ * ends.  The call allocates nothing.  Plans whose workspace
+ * (gdn_chunk_fwd_seq_workspace_bytes) exceeds 64 MiB return
+ * GDN_ERR_WORKSPACE and write nothing.  Nothing in the array needs to start
+ * at zero (every byte a call reads was written earlier in the same call),
+ * and it keeps the last call's contents.  Calls that overlap on one GPU
+ * (two streams, two threads) share that array and race: serialize them.
+ * Runs on the current device.  Everything else as gdn_chunk_fwd_seq.
+ */
+gdn_status gdn_chunk_fwd_seq_noalloc(const gdn_shape* s, int seg_chunks,
+                                     const void* q, const void* k, const void* v,
+                                     const float* alpha, const float* beta, const float* eta,
+                                     const float* S0, void* O, float* S_final,
+                                     void* stream);
+
+/*
  * The same pass with bf16 inputs through the split-bf16 kernels: every
  * derived matrix-product operand is a pair of bf16 numbers (hi + lo, about
  * 16 significant bits), which keeps the normwise error near 1e-5 whatever

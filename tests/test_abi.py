@@ -229,3 +229,19 @@ def test_default_plan_host_logic(lib):
     assert ws(B=4, H=16, T=4096) == 0
     assert ws(B=1, H=32, T=32768, d_v=256) == 0
     assert ws(B=1, H=1, T=64) == 0
+
+
+def test_noalloc_entry_rejects_before_launch(lib):
+    """gdn_chunk_fwd_seq_noalloc checks its scratch limit (64 MiB) on the
+    host: a plan that needs more returns GDN_ERR_WORKSPACE, a negative
+    segment length GDN_ERR_BAD_SHAPE, a bad shape its own error."""
+    def call(s, seg):
+        return lib.gdn_chunk_fwd_seq_noalloc(ctypes.byref(s), seg, FAKE, FAKE, FAKE, None, FAKE,
+                                             None, None, FAKE, FAKE, None)
+    big = shape(B=1, H=1, T=200000, d_k=128, d_v=128)
+    assert lib.gdn_chunk_fwd_seq_workspace_bytes(ctypes.byref(big), 1) > 64 << 20
+    assert call(big, 1) == 5
+    assert "64 MiB" in lib.gdn_last_error().decode()
+    assert call(shape(), -1) == 2
+    assert call(shape(B=0), 0) == 2
+    assert call(shape(d_k=48), 0) == 4
