@@ -250,9 +250,9 @@ gdn_status check_launch() {
 }  // namespace
 
 namespace gdn {
-FwdLauncher fast_launcher(int C, int dk, int ns, bool eta) {
+FwdLauncher fast_launcher(int C, int dk, int ns, bool eta, bool seg) {
 #define GDN_FAST_PICK(CC, KK) \
-    if (C == CC && dk == KK) return fast_launcher_c##CC##_d##KK(ns, eta);
+    if (C == CC && dk == KK) return fast_launcher_c##CC##_d##KK(ns, eta, seg);
     GDN_FAST_PICK(16, 32)
     GDN_FAST_PICK(16, 64)
     GDN_FAST_PICK(16, 96)
@@ -318,7 +318,7 @@ gdn_status run_chunk(const gdn_shape* s, const ChunkArgs& a, Path path, void* st
     bool pipelined = false;
     if (fused) {
         nw = plan.ns;
-        launch = gdn::fast_launcher(s->chunk_size, s->d_k, nw, a.eta != nullptr);
+        launch = gdn::fast_launcher(s->chunk_size, s->d_k, nw, a.eta != nullptr, plan.nseg > 1);
         pipelined = true;
     } else if (bf && pipe_shape(*s)) {
         nw = choose_scan_waves(*s);

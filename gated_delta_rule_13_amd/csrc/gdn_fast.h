@@ -199,7 +199,9 @@ struct FastRoles {
     static constexpr int nseg(int w) { return seg(w, 0) < 0 ? 0 : seg(w, 1) < 0 ? 1 : 2; }
 };
 
-template <int C, int DK, int NS, bool ETA>
+// SEG: the sequence-parallel launch (segments, transition tiles); without
+// it every segment-related quantity folds to the plain form at compile time.
+template <int C, int DK, int NS, bool ETA, bool SEG>
 __global__ __launch_bounds__((NS + fast_prep_waves(NS)) * 64) void gdn_fwd_fast_kernel(FwdParams p) {
     using R = FastRoles<NS, C / 16>;
     constexpr int NP = R::NP;
@@ -237,17 +239,17 @@ __global__ __launch_bounds__((NS + fast_prep_waves(NS)) * 64) void gdn_fwd_fast_
         tile = blockIdx.x % p.n_tiles;
         unit = blockIdx.x / p.n_tiles;
     }
-    const int nseg = p.nseg;
+    const int nseg = SEG ? p.nseg : 1;
     // padding workgroups of an XCD-grouped grid (units rounded up to a
     // multiple of 8) have none: they leave before any barrier, and so do the
     // transition tiles of a first segment (it starts from the true state)
     if (unit >= p.B * p.H * nseg) return;
-    const int bh = unit / nseg, seg = unit - bh * nseg;
-    const bool trans = tile >= p.n_tiles_v;
+    const int bh = SEG ? unit / nseg : unit, seg = SEG ? unit - bh * nseg : 0;
+    const bool trans = SEG && tile >= p.n_tiles_v;
     if (trans && seg == 0) return;
     // this segment's tokens: T from token tbase of the sequence
-    const int tbase = seg * p.seg_len;
-    const int T = min(p.T - tbase, p.seg_len), dv = p.dv;
+    const int tbase = SEG ? seg * p.seg_len : 0;
+    const int T = SEG ? min(p.T - tbase, p.seg_len) : p.T, dv = p.dv;
     const size_t tok0 = (size_t)bh * p.T + tbase;
     const int nchunks = (T + C - 1) / C;
     const __bf16* kb = reinterpret_cast<const __bf16*>(p.k) + tok0 * DK;
@@ -627,7 +629,7 @@ __global__ __launch_bounds__((NS + fast_prep_waves(NS)) * 64) void gdn_fwd_fast_
         const size_t sb = (size_t)bh * dv * DK + (size_t)(col0 + n) * DK;
         const float* s0p = (seg == 0 && p.S0) ? p.S0 + sb : nullptr;
         const size_t seg_base = ((size_t)bh * nseg + seg) * (dv + DK) * DK;
-        float* sfp = nseg == 1 ? p.S_final + sb
+        float* sfp = !SEG  ? p.S_final + sb
                      : trans   ? p.seg_state + seg_base + (size_t)dv * DK + col0 + n
                                : p.seg_state + seg_base + (size_t)(col0 + n) * DK;
         const int sst = trans ? DK : 1;

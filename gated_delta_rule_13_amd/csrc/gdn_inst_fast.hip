@@ -12,18 +12,20 @@
 
 namespace gdn {
 namespace {
-template <int NS, bool ETA>
+template <int NS, bool ETA, bool SEG>
 void launch(const FwdParams& p, long nblocks, hipStream_t st) {
-    hipLaunchKernelGGL((gdn_fwd_fast_kernel<GDN_C, GDN_DK, NS, ETA>), dim3((unsigned)nblocks),
+    hipLaunchKernelGGL((gdn_fwd_fast_kernel<GDN_C, GDN_DK, NS, ETA, SEG>), dim3((unsigned)nblocks),
                        dim3((NS + fast_prep_waves(NS)) * 64), 0, st, p);
 }
 }  // namespace
 
-FwdLauncher GDN_NAME(GDN_C, GDN_DK)(int ns, bool eta) {
+// (the sequence-parallel form runs one scan wave per workgroup only)
+FwdLauncher GDN_NAME(GDN_C, GDN_DK)(int ns, bool eta, bool seg) {
+    if (seg) return ns == 1 ? (eta ? launch<1, true, true> : launch<1, false, true>) : nullptr;
     switch (ns) {
-        case 1: return eta ? launch<1, true> : launch<1, false>;
-        case 2: return eta ? launch<2, true> : launch<2, false>;
-        case 4: return eta ? launch<4, true> : launch<4, false>;
+        case 1: return eta ? launch<1, true, false> : launch<1, false, false>;
+        case 2: return eta ? launch<2, true, false> : launch<2, false, false>;
+        case 4: return eta ? launch<4, true, false> : launch<4, false, false>;
     }
     return nullptr;
 }
