@@ -29,6 +29,22 @@ def lib():
     return _lib.load()
 
 
+@pytest.fixture
+def lib_nogpu(lib):
+    """The library, for calls with fake device pointers: every such call
+    must fail validation before any launch.  Where a GPU is visible they are
+    skipped, so that a validation regression can never launch a kernel on
+    those addresses."""
+    try:
+        import torch
+        visible = torch.cuda.device_count() > 0
+    except Exception:
+        visible = False
+    if visible:
+        pytest.skip("calls with fake device pointers run only where no GPU is visible")
+    return lib
+
+
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
@@ -74,25 +90,29 @@ def fwd(lib, s, **ptrs):
     (dict(qkv_dtype=1, d_k=96), 4), (dict(d_k=16, chunk_size=8), 4),
     (dict(T=5_000_000), 4),
 ])
-def test_bad_shapes_rejected(lib, kw, expected):
+def test_bad_shapes_rejected(lib_nogpu, kw, expected):
+    lib = lib_nogpu
     # a mismatched q pointer (odd address) could never reach a launch either
     assert fwd(lib, shape(**kw), q=ctypes.c_void_p(0x10001)) == expected
     assert lib.gdn_last_error().decode() != ""
     assert lib.gdn_chunk_fwd_workspace_bytes(ctypes.byref(shape(**kw))) == ctypes.c_size_t(-1).value
 
 
-def test_null_arguments_rejected(lib):
+def test_null_arguments_rejected(lib_nogpu):
+    lib = lib_nogpu
     assert fwd(lib, None) == 1
     for name in ("q", "k", "v", "beta", "O", "S"):
         assert fwd(lib, shape(), **{name: None}) == 1, name
 
 
-def test_misaligned_pointers_rejected(lib):
+def test_misaligned_pointers_rejected(lib_nogpu):
+    lib = lib_nogpu
     for name in ("q", "k", "v", "beta", "O", "S", "alpha", "S0"):
         assert fwd(lib, shape(), **{name: ctypes.c_void_p(0x10004)}) == 4, name
 
 
-def test_prep_validation(lib):
+def test_prep_validation(lib_nogpu):
+    lib = lib_nogpu
     s = shape()
     assert lib.gdn_chunk_prep(None, FAKE, FAKE, None, FAKE, None, None, None, None, 0, None) == 1
     assert lib.gdn_chunk_prep(ctypes.byref(shape(B=0)), FAKE, FAKE, None, FAKE, FAKE, None, None,
@@ -104,8 +124,9 @@ def test_prep_validation(lib):
                               None, 0, None) == 0
 
 
-def test_new_entries_validate(lib):
+def test_new_entries_validate(lib_nogpu):
     """gdn_chunk_fwd_precise and gdn_chunk_fwd_stages reject before any launch."""
+    lib = lib_nogpu
     sp = ctypes.byref(shape())
     odd = ctypes.c_void_p(0x10001)
     assert lib.gdn_chunk_fwd_precise(None, FAKE, FAKE, FAKE, None, FAKE, None, None, FAKE, FAKE,
@@ -163,14 +184,16 @@ def rec(lib, s, **ptrs):
     (dict(B=0), 2), (dict(T=0), 2), (dict(d_v=0), 2), (dict(qkv_dtype=5), 3),
     (dict(d_k=48), 4), (dict(d_k=512), 4), (dict(d_v=70000), 4),
 ])
-def test_recurrent_bad_shapes_rejected(lib, kw, expected):
+def test_recurrent_bad_shapes_rejected(lib_nogpu, kw, expected):
+    lib = lib_nogpu
     # an odd q pointer as well: even a shape check that wrongly passed could
     # not reach a launch
     assert rec(lib, shape(**kw), q=ctypes.c_void_p(0x10001)) == expected
     assert lib.gdn_last_error().decode() != ""
 
 
-def test_recurrent_null_and_misaligned_rejected(lib):
+def test_recurrent_null_and_misaligned_rejected(lib_nogpu):
+    lib = lib_nogpu
     assert rec(lib, None) == 1
     for name in ("q", "k", "v", "beta", "O", "S"):
         assert rec(lib, shape(), **{name: None}) == 1, name
@@ -185,10 +208,11 @@ def seq(lib, s, seg_chunks, ws=None, ws_bytes=0, **ptrs):
                                  p["beta"], p["eta"], p["S0"], p["O"], p["S"], ws, ws_bytes, None)
 
 
-def test_seq_entry_validates(lib):
+def test_seq_entry_validates(lib_nogpu):
     """gdn_chunk_fwd_seq rejects before any launch: a negative segment
     length, segments of fp32 inputs, a missing, short or misaligned
     workspace."""
+    lib = lib_nogpu
     big = ctypes.c_size_t(-1).value
     s = shape(T=300)
     assert seq(lib, s, -1) == 2
@@ -231,10 +255,11 @@ def test_default_plan_host_logic(lib):
     assert ws(B=1, H=1, T=64) == 0
 
 
-def test_noalloc_entry_rejects_before_launch(lib):
+def test_noalloc_entry_rejects_before_launch(lib_nogpu):
     """gdn_chunk_fwd_seq_noalloc checks its scratch limit (64 MiB) on the
     host: a plan that needs more returns GDN_ERR_WORKSPACE, a negative
     segment length GDN_ERR_BAD_SHAPE, a bad shape its own error."""
+    lib = lib_nogpu
     def call(s, seg):
         return lib.gdn_chunk_fwd_seq_noalloc(ctypes.byref(s), seg, FAKE, FAKE, FAKE, None, FAKE,
                                              None, None, FAKE, FAKE, None)
