@@ -28,28 +28,38 @@ bool fast_pair(int C, int dk) {
     return dk == 256 && C <= 32;
 }
 
-// Shapes some kernel covers.  bf16: C in {16, 32, 64} with d_k in
-// {32, 64, 96, 128}, d_k 256 with C <= 32 (the fast path; d_k 16 is not
-// built: the bf16 and fp16 MFMAs take 32 elements per k-step, and fp32
-// inputs cover d_k 16); f32: C in {16, 32, 64} with d_k in
-// {16, 32, 64, 128}, d_k 256 with C <= 32 (the generic kernel; C 64 with
-// d_k 256 would need more than the 160 KB of LDS).  d_v: multiple of 16 in
+// The shape the kernels run: at d_k 256 a 64-token chunk is computed as two
+// 32-token chunks (64-token tiles of d_k 256 would need more than the
+// 160 KB of LDS).  The chunk length only groups the same recurrence, so the
+// result is the same function of the inputs, up to rounding.
+gdn_shape compute_shape(const gdn_shape& s) {
+    gdn_shape c = s;
+    if (s.d_k == 256 && s.chunk_size == 64) c.chunk_size = 32;
+    return c;
+}
+
+// Shapes some kernel covers (checked on the compute shape).  bf16: C in
+// {16, 32, 64} with d_k in {32, 64, 96, 128, 256} (the fast path; d_k 16
+// is not built: the bf16 and fp16 MFMAs take 32 elements per k-step, and
+// fp32 inputs cover d_k 16); f32: C in {16, 32, 64} with d_k in
+// {16, 32, 64, 128, 256} (the generic kernel).  d_v: multiple of 16 in
 // [16, 1024].
-bool supported(const gdn_shape& s, std::string* why) {
-    if (s.chunk_size != 16 && s.chunk_size != 32 && s.chunk_size != 64) {
+bool supported(const gdn_shape& s0, std::string* why) {
+    if (s0.chunk_size != 16 && s0.chunk_size != 32 && s0.chunk_size != 64) {
         *why = "chunk_size must be 16, 32 or 64";
         return false;
     }
+    const gdn_shape s = compute_shape(s0);
     if (s.qkv_dtype == GDN_BF16) {
         if (!fast_pair(s.chunk_size, s.d_k)) {
-            *why = "bf16 inputs need d_k in {32, 64, 96, 128}, or 256 with chunk_size <= 32";
+            *why = "bf16 inputs need d_k in {32, 64, 96, 128, 256}";
             return false;
         }
     } else {
         const bool dk_ok = s.d_k == 16 || s.d_k == 32 || s.d_k == 64 || s.d_k == 128 ||
                            (s.d_k == 256 && s.chunk_size <= 32);
         if (!dk_ok) {
-            *why = "f32 inputs need d_k in {16, 32, 64, 128}, or 256 with chunk_size <= 32";
+            *why = "f32 inputs need d_k in {16, 32, 64, 128, 256}";
             return false;
         }
     }
@@ -287,11 +297,15 @@ struct ChunkArgs {
 
 // seg_chunks: < 0 the plain form only; 0 the default plan; > 0 that many
 // chunks per segment (default path, fused kernel).
-gdn_status run_chunk(const gdn_shape* s, const ChunkArgs& a, Path path, void* stream,
+gdn_status run_chunk(const gdn_shape* s_in, const ChunkArgs& a, Path path, void* stream,
                      int seg_chunks = -1, void* workspace = nullptr, size_t workspace_bytes = 0) {
     g_last_error.clear();
-    gdn_status st = validate_shape(s);
+    gdn_status st = validate_shape(s_in);
     if (st != GDN_OK) return st;
+    const gdn_shape cs = compute_shape(*s_in);
+    const gdn_shape* s = &cs;
+    // (segment lengths count the caller's chunks)
+    if (seg_chunks > 0) seg_chunks *= s_in->chunk_size / cs.chunk_size;
     if (!a.q || !a.k || !a.v || !a.beta || !a.O || !a.S_final)
         return fail(GDN_ERR_NULL_ARG, "q, k, v, beta, O and S_final are required");
     if (!aligned16(a.q) || !aligned16(a.k) || !aligned16(a.v) || !aligned16(a.O) ||
@@ -458,7 +472,8 @@ size_t gdn_chunk_fwd_seq_workspace_bytes(const gdn_shape* s, int seg_chunks) {
         return (size_t)-1;
     }
     if (s->qkv_dtype != GDN_BF16) return 0;
-    return make_plan(*s, seg_chunks).bytes;
+    const gdn_shape cs = compute_shape(*s);
+    return make_plan(cs, seg_chunks * (s->chunk_size / cs.chunk_size)).bytes;
 }
 
 gdn_status gdn_chunk_fwd_seq(const gdn_shape* s, int seg_chunks, const void* q, const void* k,
@@ -529,6 +544,11 @@ gdn_status gdn_chunk_fwd_stages(const gdn_shape* s, const void* q, const void* k
                                 float* Vp_out, void* stream) {
     if (s && s->qkv_dtype != GDN_BF16) {
         g_last_error = "stage outputs exist for bf16 inputs only";
+        return GDN_ERR_UNSUPPORTED;
+    }
+    if (s && s->d_k == 256 && s->chunk_size == 64) {
+        // (T per chunk is laid out by the caller's chunk length)
+        g_last_error = "stage outputs at d_k 256 need chunk_size <= 32";
         return GDN_ERR_UNSUPPORTED;
     }
     return run_chunk(s, ChunkArgs{q, k, v, alpha, beta, eta, S0, O, S_final, T_out, Vp_out},

@@ -63,13 +63,15 @@ typedef struct {
  * Supported combinations (anything else that is well-formed returns
  * GDN_ERR_UNSUPPORTED):
  *   chunk_size in {16, 32, 64};
- *   qkv_dtype GDN_BF16: d_k in {32, 64, 96, 128}, or d_k = 256 with
- *                       chunk_size in {16, 32} (d_k 16 is not built: the bf16
- *                       and fp16 MFMAs take 32 elements per k-step; fp32
- *                       inputs cover it);
- *   qkv_dtype GDN_F32:  d_k in {16, 32, 64, 128}, or d_k = 256 with
- *                       chunk_size in {16, 32} (chunk 64 at d_k 256 would need
- *                       more than the 160 KB of LDS of one compute unit);
+ *   qkv_dtype GDN_BF16: d_k in {32, 64, 96, 128, 256} (d_k 16 is not built:
+ *                       the bf16 and fp16 MFMAs take 32 elements per k-step;
+ *                       fp32 inputs cover it);
+ *   qkv_dtype GDN_F32:  d_k in {16, 32, 64, 128, 256};
+ *   at d_k 256 a chunk of 64 tokens is computed as two chunks of 32 (its
+ *   64-token tiles would need more than the 160 KB of LDS of one compute
+ *   unit): the same recurrence grouped differently, so the same result up
+ *   to rounding (gdn_chunk_fwd_stages, whose T is laid out per chunk, and
+ *   gdn_chunk_prep reject that case);
  *   d_v a multiple of 16 in [16, 1024]; one head's largest tensor (T x
  *   max(d_k, d_v) x 4 bytes) below 2 GiB.
  * T may be any value >= 1; a last chunk shorter than chunk_size is handled

@@ -84,9 +84,9 @@ def fwd(lib, s, **ptrs):
 @pytest.mark.parametrize("kw,expected", [
     (dict(B=0), 2), (dict(H=-1), 2), (dict(T=0), 2), (dict(d_k=0), 2),
     (dict(qkv_dtype=7), 3), (dict(o_dtype=-1), 3),
-    (dict(chunk_size=48), 4), (dict(d_k=256), 4), (dict(d_k=16), 4), (dict(d_k=8), 4),
+    (dict(chunk_size=48), 4), (dict(d_k=512), 4), (dict(d_k=16), 4), (dict(d_k=8), 4),
     (dict(d_k=48), 4),
-    (dict(d_v=40), 4), (dict(d_v=2048), 4), (dict(qkv_dtype=1, d_k=256), 4),
+    (dict(d_v=40), 4), (dict(d_v=2048), 4), (dict(qkv_dtype=1, d_k=192), 4),
     (dict(qkv_dtype=1, d_k=96), 4), (dict(d_k=16, chunk_size=8), 4),
     (dict(T=5_000_000), 4),
 ])
@@ -144,13 +144,18 @@ def test_new_entries_validate(lib_nogpu):
     f32 = ctypes.byref(shape(qkv_dtype=1, d_k=64))
     assert lib.gdn_chunk_fwd_stages(f32, FAKE, FAKE, FAKE, None, FAKE, None, None, FAKE, FAKE,
                                     None, None, None) == 4
+    # d_k 256 at chunk 64 runs as 32-token chunks: no per-chunk T of 64 to give
+    d256 = ctypes.byref(shape(d_k=256))
+    assert lib.gdn_chunk_fwd_stages(d256, FAKE, FAKE, FAKE, None, FAKE, None, None, FAKE, FAKE,
+                                    None, None, None) == 4
 
 
 
 def test_workspace_query_and_strings(lib):
     for kw in (dict(), dict(qkv_dtype=1, d_k=16, d_v=16, chunk_size=16),
                dict(chunk_size=32), dict(d_v=256), dict(chunk_size=16), dict(d_k=96, d_v=192),
-               dict(qkv_dtype=1, d_k=128), dict(qkv_dtype=1, d_k=256, chunk_size=32)):
+               dict(qkv_dtype=1, d_k=128), dict(qkv_dtype=1, d_k=256, chunk_size=32),
+               dict(d_k=256), dict(qkv_dtype=1, d_k=256)):
         assert lib.gdn_chunk_fwd_workspace_bytes(ctypes.byref(shape(**kw))) == 0
     for code in range(7):
         assert lib.gdn_status_string(code).decode()

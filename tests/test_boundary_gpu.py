@@ -1,5 +1,6 @@
 """The rest of the shape matrix the boundary accepts: fp32 inputs with
-d_k 128 and 256 (on the generic kernel),
+d_k 128 and 256 (on the generic kernel), and d_k 256 with 64-token chunks
+(bf16 and fp32; computed as 32-token chunks),
 through gdn_chunk_fwd, gdn_chunk_fwd_eta and gdn_chunk_fwd_precise, every
 (b, h) sequence against the fp64 oracle, with NaN-prefilled outputs; and
 the stage kernel's T, W, U at the new shapes against the pages' chunk
@@ -26,6 +27,8 @@ SHAPES = [
     ("f32", 1, 2, 70, 256, 64, 32),
     ("f32", 1, 1, 45, 256, 48, 16),
     ("f32", 8, 8, 100, 128, 64, 32),    # 64 heads: several waves per workgroup
+    ("f32", 1, 2, 150, 256, 64, 64),    # chunk 64 at d_k 256: run as 32-token chunks
+    ("bf16", 1, 2, 150, 256, 64, 64),
 ]
 
 
