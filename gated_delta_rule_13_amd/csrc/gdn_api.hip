@@ -24,7 +24,7 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 // Built shapes of the default (fp16-operand) path for bf16 inputs.
 bool fast_pair(int C, int dk) {
     if (C != 16 && C != 32 && C != 64) return false;
-    if (dk == 32 || dk == 64 || dk == 96 || dk == 128) return true;
+    if (dk == 16 || dk == 32 || dk == 64 || dk == 96 || dk == 128) return true;
     return dk == 256 && C <= 32;
 }
 
@@ -39,11 +39,10 @@ gdn_shape compute_shape(const gdn_shape& s) {
 }
 
 // Shapes some kernel covers (checked on the compute shape).  bf16: C in
-// {16, 32, 64} with d_k in {32, 64, 96, 128, 256} (the fast path; d_k 16
-// is not built: the bf16 and fp16 MFMAs take 32 elements per k-step, and
-// fp32 inputs cover d_k 16); f32: C in {16, 32, 64} with d_k in
-// {16, 32, 64, 128, 256} (the generic kernel).  d_v: multiple of 16 in
-// [16, 1024].
+// {16, 32, 64} with d_k in {16, 32, 64, 96, 128, 256} (the fast path; d_k
+// 16 runs zero-padded on the d_k 32 kernel); f32: C in {16, 32, 64} with
+// d_k in {16, 32, 64, 128, 256} (the generic kernel).  d_v: multiple of 16
+// in [16, 1024].
 bool supported(const gdn_shape& s0, std::string* why) {
     if (s0.chunk_size != 16 && s0.chunk_size != 32 && s0.chunk_size != 64) {
         *why = "chunk_size must be 16, 32 or 64";
@@ -52,7 +51,7 @@ bool supported(const gdn_shape& s0, std::string* why) {
     const gdn_shape s = compute_shape(s0);
     if (s.qkv_dtype == GDN_BF16) {
         if (!fast_pair(s.chunk_size, s.d_k)) {
-            *why = "bf16 inputs need d_k in {32, 64, 96, 128, 256}";
+            *why = "bf16 inputs need d_k in {16, 32, 64, 96, 128, 256}";
             return false;
         }
     } else {
@@ -219,7 +218,9 @@ Plan make_plan(const gdn_shape& s, int seg_chunks) {
     pl.seg_len = s.T;
     const long nchunks = (s.T + s.chunk_size - 1) / s.chunk_size;
     int best_L = 0;
-    if (seg_chunks > 0) {
+    if (s.d_k < 32) {
+        // (no segments at d_k 16: its kernel runs zero-padded)
+    } else if (seg_chunks > 0) {
         if (seg_chunks < nchunks) best_L = seg_chunks;
     } else {
         const long bh = (long)s.B * s.H;
@@ -263,6 +264,9 @@ namespace gdn {
 FwdLauncher fast_launcher(int C, int dk, int ns, bool eta, bool seg) {
 #define GDN_FAST_PICK(CC, KK) \
     if (C == CC && dk == KK) return fast_launcher_c##CC##_d##KK(ns, eta, seg);
+    GDN_FAST_PICK(16, 16)
+    GDN_FAST_PICK(32, 16)
+    GDN_FAST_PICK(64, 16)
     GDN_FAST_PICK(16, 32)
     GDN_FAST_PICK(16, 64)
     GDN_FAST_PICK(16, 96)
@@ -321,6 +325,8 @@ gdn_status run_chunk(const gdn_shape* s_in, const ChunkArgs& a, Path path, void*
     if (seg_chunks > 0 && !fused &&
         (long)seg_chunks * s->chunk_size < (long)s->T)
         return fail(GDN_ERR_UNSUPPORTED, "segments exist on the default path with bf16 inputs only");
+    if (seg_chunks > 0 && s->d_k < 32 && (long)seg_chunks * s->chunk_size < (long)s->T)
+        return fail(GDN_ERR_UNSUPPORTED, "segments need d_k >= 32");
     if (plan.nseg > 1) {
         if (!workspace || workspace_bytes < plan.bytes)
             return fail(GDN_ERR_WORKSPACE, "workspace smaller than gdn_chunk_fwd_workspace_bytes");

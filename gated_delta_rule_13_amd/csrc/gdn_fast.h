@@ -201,7 +201,11 @@ struct FastRoles {
 
 // SEG: the sequence-parallel launch (segments, transition tiles); without
 // it every segment-related quantity folds to the plain form at compile time.
-template <int C, int DK, int NS, bool ETA, bool SEG>
+// DKG: the d_k of the tensors in memory when it is smaller than the
+// kernel's (d_k 16 runs as 32: the MFMAs take 32 elements per k-step): the
+// keys and queries are padded with zeros as they are staged and the state's
+// extra rows stay zero, so the products are those of d_k = DKG.
+template <int C, int DK, int NS, bool ETA, bool SEG, int DKG = DK>
 __global__ __launch_bounds__((NS + fast_prep_waves(NS)) * 64) void gdn_fwd_fast_kernel(FwdParams p) {
     using R = FastRoles<NS, C / 16>;
     constexpr int NP = R::NP;
@@ -252,14 +256,15 @@ __global__ __launch_bounds__((NS + fast_prep_waves(NS)) * 64) void gdn_fwd_fast_
     const int T = SEG ? min(p.T - tbase, p.seg_len) : p.T, dv = p.dv;
     const size_t tok0 = (size_t)bh * p.T + tbase;
     const int nchunks = (T + C - 1) / C;
-    const __bf16* kb = reinterpret_cast<const __bf16*>(p.k) + tok0 * DK;
-    const __bf16* qb = reinterpret_cast<const __bf16*>(p.q) + tok0 * DK;
+    static_assert(DKG == DK || (DKG == 16 && DK == 32 && !SEG), "padded d_k");
+    const __bf16* kb = reinterpret_cast<const __bf16*>(p.k) + tok0 * DKG;
+    const __bf16* qb = reinterpret_cast<const __bf16*>(p.q) + tok0 * DKG;
     const __bf16* vb = reinterpret_cast<const __bf16*>(p.v) + tok0 * dv;
     const float* ab = p.alpha ? p.alpha + tok0 : nullptr;
     const float* bb = p.beta + tok0;
     const float* eb = p.eta ? p.eta + tok0 : nullptr;
-    const buf_t kbuf = buffer_over(kb, (uint32_t)T * DK * 2);
-    const buf_t qbuf = buffer_over(qb, (uint32_t)T * DK * 2);
+    const buf_t kbuf = buffer_over(kb, (uint32_t)T * DKG * 2);
+    const buf_t qbuf = buffer_over(qb, (uint32_t)T * DKG * 2);
     // scan waves: first value column (transition tiles: first transition row)
     const int col0 = (trans ? tile - p.n_tiles_v : tile) * DVT + 16 * wave;
 
@@ -284,9 +289,11 @@ __global__ __launch_bounds__((NS + fast_prep_waves(NS)) * 64) void gdn_fwd_fast_
                 const int vi = plane + i * 64 * NSTG;
                 if (i + 1 < NKV || vi < KV) {
                     const int r = vi / (DK / 8), u = vi % (DK / 8);
-                    const uint32_t off = 2u * ((t0 + r) * DK + 32 * (u >> 2) + 4 * (u & 3));
-                    const uint2 k0 = buf_load_8B(kbuf, off), k1 = buf_load_8B(kbuf, off + 32);
-                    const uint2 q0 = buf_load_8B(qbuf, off), q1 = buf_load_8B(qbuf, off + 32);
+                    const uint32_t off = 2u * ((t0 + r) * DKG + 32 * (u >> 2) + 4 * (u & 3));
+                    const uint2 k0 = buf_load_8B(kbuf, off), q0 = buf_load_8B(qbuf, off);
+                    // (d_k 16 padded to 32: the second pieces are the zero padding)
+                    const uint2 k1 = DKG == DK ? buf_load_8B(kbuf, off + 32) : make_uint2(0, 0);
+                    const uint2 q1 = DKG == DK ? buf_load_8B(qbuf, off + 32) : make_uint2(0, 0);
                     stK[i] = make_uint4(k0.x, k0.y, k1.x, k1.y);
                     stQ[i] = make_uint4(q0.x, q0.y, q1.x, q1.y);
                 }
@@ -626,7 +633,7 @@ __global__ __launch_bounds__((NS + fast_prep_waves(NS)) * 64) void gdn_fwd_fast_
         // identity rows (transition tiles); end state: S_final, or this
         // segment's rows of seg_state (transition rows stored transposed,
         // element (row, k) at k * d_k + row)
-        const size_t sb = (size_t)bh * dv * DK + (size_t)(col0 + n) * DK;
+        const size_t sb = (size_t)bh * dv * DKG + (size_t)(col0 + n) * DKG;
         const float* s0p = (seg == 0 && p.S0) ? p.S0 + sb : nullptr;
         const size_t seg_base = ((size_t)bh * nseg + seg) * (dv + DK) * DK;
         float* sfp = !SEG  ? p.S_final + sb
@@ -638,7 +645,7 @@ __global__ __launch_bounds__((NS + fast_prep_waves(NS)) * 64) void gdn_fwd_fast_
 #pragma unroll
             for (int j = 0; j < 4; ++j)
                 Sacc[t][j] = trans ? (col0 + n == 16 * t + 4 * h + j ? 1.f : 0.f)
-                                   : s0p ? s0p[16 * t + 4 * h + j] : 0.f;
+                             : (s0p && 16 * t < DKG) ? s0p[16 * t + 4 * h + j] : 0.f;
         v_load(0);
         // wait here for the initial state (and the first values): at the loop
         // head the state registers must not look like pending loads, or every
@@ -861,7 +868,8 @@ __global__ __launch_bounds__((NS + fast_prep_waves(NS)) * 64) void gdn_fwd_fast_
 #pragma unroll
         for (int t = 0; t < NK; ++t)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) sfp[(16 * t + 4 * h + j) * sst] = Sacc[t][j];
+            for (int j = 0; j < 4; ++j)
+                if (16 * t < DKG) sfp[(16 * t + 4 * h + j) * sst] = Sacc[t][j];
     }
 }
 

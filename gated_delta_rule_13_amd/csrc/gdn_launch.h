@@ -16,12 +16,15 @@ using RecLauncher = void (*)(const RecParams&, long nblocks, hipStream_t);
 using SeqLauncher = void (*)(const SeqParams&, hipStream_t);
 
 // fp16-operand fused kernel (bf16 inputs): C in {16, 32, 64}, d_k in
-// {32, 64, 96, 128} (and 256 with C <= 32), ns scan waves in {1, 2, 4};
+// {16, 32, 64, 96, 128} (and 256 with C <= 32), ns scan waves in {1, 2, 4};
 // seg: the sequence-parallel launch (ns = 1 only).  Null when the shape is
 // not built.  One definition per (C, d_k), in the object built from
 // gdn_inst_fast.hip with that pair.
 FwdLauncher fast_launcher(int C, int dk, int ns, bool eta, bool seg);
 #define GDN_FAST_DECL(CC, KK) FwdLauncher fast_launcher_c##CC##_d##KK(int ns, bool eta, bool seg);
+GDN_FAST_DECL(16, 16)
+GDN_FAST_DECL(32, 16)
+GDN_FAST_DECL(64, 16)
 GDN_FAST_DECL(16, 32)
 GDN_FAST_DECL(16, 64)
 GDN_FAST_DECL(16, 96)

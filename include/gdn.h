@@ -63,9 +63,10 @@ typedef struct {
  * Supported combinations (anything else that is well-formed returns
  * GDN_ERR_UNSUPPORTED):
  *   chunk_size in {16, 32, 64};
- *   qkv_dtype GDN_BF16: d_k in {32, 64, 96, 128, 256} (d_k 16 is not built:
- *                       the bf16 and fp16 MFMAs take 32 elements per k-step;
- *                       fp32 inputs cover it);
+ *   qkv_dtype GDN_BF16: d_k in {16, 32, 64, 96, 128, 256} (d_k 16 runs on
+ *                       the d_k 32 kernel with the keys and queries padded
+ *                       with zeros as they are staged: the MFMAs take 32
+ *                       elements per k-step; no sequence-parallel segments);
  *   qkv_dtype GDN_F32:  d_k in {16, 32, 64, 128, 256};
  *   at d_k 256 a chunk of 64 tokens is computed as two chunks of 32 (its
  *   64-token tiles would need more than the 160 KB of LDS of one compute

@@ -84,7 +84,7 @@ def fwd(lib, s, **ptrs):
 @pytest.mark.parametrize("kw,expected", [
     (dict(B=0), 2), (dict(H=-1), 2), (dict(T=0), 2), (dict(d_k=0), 2),
     (dict(qkv_dtype=7), 3), (dict(o_dtype=-1), 3),
-    (dict(chunk_size=48), 4), (dict(d_k=512), 4), (dict(d_k=16), 4), (dict(d_k=8), 4),
+    (dict(chunk_size=48), 4), (dict(d_k=512), 4), (dict(d_k=80), 4), (dict(d_k=8), 4),
     (dict(d_k=48), 4),
     (dict(d_v=40), 4), (dict(d_v=2048), 4), (dict(qkv_dtype=1, d_k=192), 4),
     (dict(qkv_dtype=1, d_k=96), 4), (dict(d_k=16, chunk_size=8), 4),

@@ -1,6 +1,6 @@
 """The default bf16 path (fp16-operand fused kernel) beyond the workloads:
 its own intermediates against the pages' chunk matrices, the wider shape
-matrix (16-token chunks, d_k 32 / 96 / 256, the Olmo-Hybrid head shape), and
+matrix (16-token chunks, d_k 16 / 32 / 96 / 256, the Olmo-Hybrid head shape), and
 the split-bf16 alternative, gdn_chunk_fwd_precise, where the fast path's
 error grows (ungated reflections over long sequences).
 
@@ -54,6 +54,7 @@ STAGE_TOL = 4e-3
     (1, 1, 70, 64, 32, 32),
     (1, 2, 45, 64, 48, 16),
     (4, 16, 130, 128, 128, 64),  # two scan waves per workgroup
+    (1, 2, 100, 16, 32, 32),     # d_k 16, zero-padded
 ])
 def test_stages_match_chunk_matrices(B, H, T, dk, dv, C):
     x = make_random(B, H, T, dk, dv, dtype="bf16", chunk=C, seed=T + C, s0_std=0.02,
@@ -122,6 +123,10 @@ NEW_SHAPES = [
     (1, 2, 150, 256, 64, 32),
     (1, 1, 70, 256, 128, 16),
     (16, 16, 65, 64, 64, 16),     # four scan waves, 16-token chunks
+    (1, 2, 150, 16, 64, 64),      # d_k 16: zero-padded to the d_k 32 kernel
+    (1, 3, 97, 16, 32, 32),
+    (2, 2, 70, 16, 48, 16),
+    (8, 16, 130, 16, 64, 64),     # d_k 16 with two scan waves
 ]
 
 
