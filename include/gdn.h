@@ -202,7 +202,7 @@ gdn_status gdn_chunk_fwd_seq_noalloc(const gdn_shape* s, int seg_chunks,
  * the gates, at roughly twice the run time of gdn_chunk_fwd.  Shapes: bf16
  * with chunk_size in {32, 64} and d_k in {64, 128} take the pipelined
  * split kernel, bf16 d_k 32 and all f32 shapes the generic one (the other
- * bf16 shapes, chunk_size 16 or d_k 96 / 256, return GDN_ERR_UNSUPPORTED).
+ * bf16 shapes, chunk_size 16 or d_k 16 / 96 / 256, return GDN_ERR_UNSUPPORTED).
  * eta may
  * be NULL (eta = beta).  Arguments and conventions as gdn_chunk_fwd_eta,
  * without a workspace.
