@@ -53,7 +53,11 @@ __device__ __forceinline__ SplitA split_a(const float* row) {
     split8(*reinterpret_cast<const f32x4*>(row), *reinterpret_cast<const f32x4*>(row + 4), a.hi, a.lo);
     return a;
 }
-__device__ __forceinline__ f32x4 mfma_split(const SplitA& a, const f32x4& b0, const f32x4& b1, f32x4 acc) {
+// The B operand is pinned where it is used (an empty asm that the compiler
+// must treat as redefining it), so that its conversion, and with it the wait
+// for its load, is not hoisted ahead of earlier work.
+__device__ __forceinline__ f32x4 mfma_split(const SplitA& a, f32x4 b0, f32x4 b1, f32x4 acc) {
+    asm volatile("" : "+v"(b0), "+v"(b1));
     bf16x8 bh, bl;
     split8(b0, b1, bh, bl);
     acc = mfma_bf16(a.hi, bh, acc);
@@ -121,33 +125,18 @@ __global__ __launch_bounds__(256) void gdn_seq_finish_kernel(SeqParams p) {
     const size_t slot_sz = (size_t)(dv + DK) * DK;
     const float* E = p.seg_state + (size_t)bh * nseg * slot_sz;
 
-    // correction operands: for token tile u of this wave, lane (n, h) holds
-    // qm[t][32 ks + 8 h .. + 7] of token t = t0 + n, and its zero-state
-    // outputs o0[t][16 rb + 4 h .. + 3]
-    f32x4 qa[TPW][NKS][2], o0[TPW];
-#pragma unroll
-    for (int u = 0; u < TPW; ++u) {
-        const int t = tb + 16 * (w + 4 * u) + n;
-        const bool live = t < te;
-        const float* qrow = p.seg_q + ((size_t)bh * T + t) * DK + 8 * h;
-#pragma unroll
-        for (int ks = 0; ks < NKS; ++ks)
-#pragma unroll
-            for (int q = 0; q < 2; ++q)
-                qa[u][ks][q] = live ? *reinterpret_cast<const f32x4*>(qrow + 32 * ks + 4 * q) : zero4();
-        const size_t off = ((size_t)bh * T + t) * dv + 16 * rb + 4 * h;
-        const float* src = p.seg_o ? p.seg_o + off : reinterpret_cast<const float*>(p.O) + off;
-        o0[u] = live ? *reinterpret_cast<const f32x4*>(src) : zero4();
-    }
-    // X_1: rows 16 rb .. of segment 0's end state, DK / 64 16-byte pieces per thread
-    constexpr int XV = (16 * DK / 4 + 255) / 256;
+    // Every load is issued up front in the order of use, unconditionally (a
+    // token past the end reads the last valid row and is zeroed after), so
+    // that each use waits only for its own loads: X_1, then the chain's
+    // operands, then the correction's.
+    // X_1: rows 16 rb .. of segment 0's end state, in 16-byte pieces
+    constexpr int XN = 16 * DK / 4, XV = (XN + 255) / 256;
     f32x4 xin[XV];
 #pragma unroll
     for (int v = 0; v < XV; ++v) {
-        const int e = threadIdx.x + 256 * v;
+        const int e = min((int)threadIdx.x + 256 * v, XN - 1);
         const int r = e / (DK / 4), c = 4 * (e - r * (DK / 4));
-        xin[v] = e < 16 * DK / 4 ? *reinterpret_cast<const f32x4*>(E + (size_t)(16 * rb + r) * DK + c)
-                                 : zero4();
+        xin[v] = *reinterpret_cast<const f32x4*>(E + (size_t)(16 * rb + r) * DK + c);
     }
     // chain operands of steps i0 .. i0 + PF - 1: rows 16 ct + n of W_i
     // (k-slices 32 ks + 8 h ..) and E0_i in accumulator layout (rows 4 h + r,
@@ -157,6 +146,7 @@ __global__ __launch_bounds__(256) void gdn_seq_finish_kernel(SeqParams p) {
         if constexpr (Sh::BLOCKED) {
 #pragma unroll
             for (int s = 0; s < PF; ++s) {
+                // (segment 1 exists whenever this kernel runs)
                 const int i = max(1, min(i0 + s, nsteps));
                 const float* Ei = E + (size_t)i * slot_sz;
                 const float* W = Ei + (size_t)dv * DK;
@@ -176,13 +166,29 @@ __global__ __launch_bounds__(256) void gdn_seq_finish_kernel(SeqParams p) {
             }
         }
     };
-    if (nsteps > 0) load_block(1);
+    load_block(1);
+    // correction operands: for token tile u of this wave, lane (n, h) holds
+    // qm[t][32 ks + 8 h .. + 7] of token t = t0 + n, and its zero-state
+    // outputs o0[t][16 rb + 4 h .. + 3]
+    f32x4 qa[TPW][NKS][2], o0[TPW];
+#pragma unroll
+    for (int u = 0; u < TPW; ++u) {
+        const int t = min(tb + 16 * (w + 4 * u) + n, te - 1);
+        const float* qrow = p.seg_q + ((size_t)bh * T + t) * DK + 8 * h;
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+            for (int q = 0; q < 2; ++q) qa[u][ks][q] = *reinterpret_cast<const f32x4*>(qrow + 32 * ks + 4 * q);
+        const size_t off = ((size_t)bh * T + t) * dv + 16 * rb + 4 * h;
+        const float* src = p.seg_o ? p.seg_o + off : reinterpret_cast<const float*>(p.O) + off;
+        o0[u] = *reinterpret_cast<const f32x4*>(src);
+    }
     __builtin_amdgcn_sched_barrier(0);   // every load above is issued before any use
 #pragma unroll
     for (int v = 0; v < XV; ++v) {
         const int e = threadIdx.x + 256 * v;
         const int r = e / (DK / 4), c = 4 * (e - r * (DK / 4));
-        if (e < 16 * DK / 4) *reinterpret_cast<f32x4*>(&X[r][c]) = xin[v];
+        if (e < XN) *reinterpret_cast<f32x4*>(&X[r][c]) = xin[v];
     }
     __syncthreads();
 
