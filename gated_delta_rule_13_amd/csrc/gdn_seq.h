@@ -48,11 +48,6 @@ struct SeqParams {
 struct SplitA {
     bf16x8 hi, lo;
 };
-__device__ __forceinline__ SplitA split_a(const float* row) {
-    SplitA a;
-    split8(*reinterpret_cast<const f32x4*>(row), *reinterpret_cast<const f32x4*>(row + 4), a.hi, a.lo);
-    return a;
-}
 // The B operand is pinned where it is used (an empty asm that the compiler
 // must treat as redefining it), so that its conversion, and with it the wait
 // for its load, is not hoisted ahead of earlier work.
@@ -102,8 +97,11 @@ template <int DK>
 __global__ __launch_bounds__(256) void gdn_seq_finish_kernel(SeqParams p) {
     using Sh = FinishShape<DK>;
     constexpr int NC = Sh::NC, NCW = Sh::NCW, NKS = Sh::NKS, PF = Sh::PF, TPW = Sh::TPW, G = Sh::G;
-    constexpr int XP = DK + 4;   // LDS row stride (floats): 16 rows x 16-byte reads spread over the banks
-    __shared__ float X[16][XP];
+    // the rows' current end state in LDS, already split into its bf16 hi and
+    // lo parts (the A operand of every product): split once where it is
+    // produced, not by every reader
+    constexpr int XP = DK + 8;   // row stride (bf16): the 16 rows' 16-byte reads spread over the banks
+    __shared__ __bf16 Xh[16][XP], Xl[16][XP];
     const int dv = p.dv, nseg = p.nseg, L = p.seg_len, T = p.T;
     const int nrb = dv / 16;
     const int ngps = (L + G - 1) / G;
@@ -122,6 +120,18 @@ __global__ __launch_bounds__(256) void gdn_seq_finish_kernel(SeqParams p) {
     const int nsteps = j - 1 + (fin ? 1 : 0);
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int n = lane & 15, h = lane >> 4;
+    auto x_put = [&](int r, int c, float v) __attribute__((always_inline)) {
+        __bf16 hi, lo;
+        split_bf16(v, hi, lo);
+        Xh[r][c] = hi;
+        Xl[r][c] = lo;
+    };
+    auto x_get = [&](int ks) __attribute__((always_inline)) {
+        SplitA a;
+        a.hi = *reinterpret_cast<const bf16x8*>(&Xh[n][32 * ks + 8 * h]);
+        a.lo = *reinterpret_cast<const bf16x8*>(&Xl[n][32 * ks + 8 * h]);
+        return a;
+    };
     const size_t slot_sz = (size_t)(dv + DK) * DK;
     const float* E = p.seg_state + (size_t)bh * nseg * slot_sz;
 
@@ -188,7 +198,10 @@ __global__ __launch_bounds__(256) void gdn_seq_finish_kernel(SeqParams p) {
     for (int v = 0; v < XV; ++v) {
         const int e = threadIdx.x + 256 * v;
         const int r = e / (DK / 4), c = 4 * (e - r * (DK / 4));
-        if (e < XN) *reinterpret_cast<f32x4*>(&X[r][c]) = xin[v];
+        if (e < XN) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) x_put(r, c + q, xin[v][q]);
+        }
     }
     __syncthreads();
 
@@ -196,7 +209,7 @@ __global__ __launch_bounds__(256) void gdn_seq_finish_kernel(SeqParams p) {
     auto correct = [&]() __attribute__((always_inline)) {
         SplitA xa[NKS];
 #pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) xa[ks] = split_a(&X[n][32 * ks + 8 * h]);
+        for (int ks = 0; ks < NKS; ++ks) xa[ks] = x_get(ks);
 #pragma unroll
         for (int u = 0; u < TPW; ++u) {
             const int t = tb + 16 * (w + 4 * u) + n;
@@ -228,7 +241,7 @@ __global__ __launch_bounds__(256) void gdn_seq_finish_kernel(SeqParams p) {
                     if (to_final)
                         p.S_final[((size_t)bh * dv + 16 * rb + 4 * h + r) * DK + 16 * ct + n] = acc[cw][r];
                     else
-                        X[4 * h + r][16 * ct + n] = acc[cw][r];
+                        x_put(4 * h + r, 16 * ct + n, acc[cw][r]);
                 }
             }
         }
@@ -247,7 +260,7 @@ __global__ __launch_bounds__(256) void gdn_seq_finish_kernel(SeqParams p) {
                 if (i == j) correct();   // (the final-state workgroup: X holds X_j)
                 SplitA xa[NKS];
 #pragma unroll
-                for (int ks = 0; ks < NKS; ++ks) xa[ks] = split_a(&X[n][32 * ks + 8 * h]);
+                for (int ks = 0; ks < NKS; ++ks) xa[ks] = x_get(ks);
                 f32x4 acc[NCW];
 #pragma unroll
                 for (int cw = 0; cw < NCW; ++cw) {
@@ -277,7 +290,7 @@ __global__ __launch_bounds__(256) void gdn_seq_finish_kernel(SeqParams p) {
                 for (int ks = 0; ks < NKS; ++ks) {
                     const f32x4 b0 = *reinterpret_cast<const f32x4*>(wrow + 32 * ks);
                     const f32x4 b1 = *reinterpret_cast<const f32x4*>(wrow + 32 * ks + 4);
-                    acc[cw] = mfma_split(split_a(&X[n][32 * ks + 8 * h]), b0, b1, acc[cw]);
+                    acc[cw] = mfma_split(x_get(ks), b0, b1, acc[cw]);
                 }
             }
             finish_step(i, acc);
