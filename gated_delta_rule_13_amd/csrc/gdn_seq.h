@@ -136,7 +136,7 @@ __global__ __launch_bounds__(256) void gdn_seq_finish_kernel(SeqParams p) {
     const float* E = p.seg_state + (size_t)bh * nseg * slot_sz;
 
     // Every load is issued up front in the order of use, unconditionally (a
-    // token past the end reads the last valid row and is zeroed after), so
+    // token past the end reads the last valid row; its output is not stored), so
     // that each use waits only for its own loads: X_1, then the chain's
     // operands, then the correction's.
     // X_1: rows 16 rb .. of segment 0's end state, in 16-byte pieces
