@@ -392,9 +392,12 @@ gdn_status run_chunk(const gdn_shape* s_in, const ChunkArgs& a, Path path, void*
     p.xcd_groups = pipelined;
     const long grid_units = pipelined ? (units + 7) / 8 * 8 : units;
     // fp32 output written through at system scope keeps the written bytes at
-    // the output size; at d_v >= 256 plain non-temporal stores measured 6 %
-    // faster (the write-back of partly written lines costs bytes, not time)
-    p.o_wt = s->d_v < 256;
+    // the output size.  Where the scan waves load their own values (the
+    // split-bf16 kernel; the fused kernel with four scan waves) their waits
+    // for those loads also wait for their earlier stores, and at d_v >= 256
+    // plain non-temporal stores measured 6 % faster there (the write-back of
+    // partly written lines costs bytes, not time).
+    p.o_wt = s->d_v < 256 || (fused && nw != 4);
     const long nblocks = grid_units * p.n_tiles;
     if (nblocks > 0x7fffffffL) return fail(GDN_ERR_BAD_SHAPE, "grid too large");
     if (finish) {

@@ -26,18 +26,22 @@
 //
 // Work is split by role inside the workgroup.  NS "scan" waves own 16 value
 // columns each and that slice of the fp32 state (S^T in MFMA accumulators);
-// four "prep" waves build chunk-local matrices one or two chunks ahead.
-// Iteration i (chunk i on the scan waves) has two phases separated by
-// workgroup barriers:
-//   phase A  scan    X_i = K_i S^T, Z^T_i = S Q_i^T
-//            prep 0  blocks of T_i below the diagonal (T_bb of chunk i and
-//                    its A blocks are from iteration i - 1)
-//            prep 1+ row strips of chunk i + 1: Gram and score tiles formed
-//                    into the diagonal blocks of A (fp32), the blocks below
-//                    them (fp16) and the masked decayed scores P (fp16)
-//   phase B  scan    Y, V' = T_i Y, state update, O = diag(exp g) Z + P V'
-//            prep 0  decay vectors of chunk i + 2; diagonal solves of chunk i + 1
-//            prep 1+ keys and queries of chunk i + 2 into LDS (fp16)
+// six "prep" waves beside one or two scan waves, four beside four (the
+// roles below are spread over them by FastRoles), build chunk-local
+// matrices one or two chunks ahead.  Iteration i (chunk i on the scan
+// waves) has two phases separated by workgroup barriers:
+//   phase A  scan     X_i = K_i S^T, Z^T_i = S Q_i^T
+//            T blocks blocks of T_i below the diagonal (T_bb of chunk i and
+//                     its A blocks are from iteration i - 1)
+//            strips   row strips of chunk i + 1: Gram and score tiles formed
+//                     into the diagonal blocks of A (fp32), the blocks below
+//                     them (fp16) and the masked decayed scores P (fp16)
+//            values   (one or two scan waves) the values of chunk i + 1
+//                     into LDS, on the solve wave
+//   phase B  scan     Y, V' = T_i Y, state update, O = diag(exp g) Z + P V'
+//            vectors  decay vectors of chunk i + 2
+//            solve    diagonal blocks T_bb of chunk i + 1
+//            staging  keys and queries of chunk i + 2 into LDS (fp16)
 // The loop starts at i = -2 so that the first two iterations only prepare.
 // The state update reads K^T straight from the token-major key tile with
 // the LDS transposing read, so the keys stay three chunks deep (chunk i for
@@ -135,6 +139,13 @@ struct alignas(16) FastLds {
     // h = 0..3), so an MFMA operand slice is one aligned 16-byte read
     _Float16 K[3][C][KP];
     _Float16 Q[2][C][KP];
+    // with one or two scan waves, the values of the scan's chunks as raw
+    // bf16 by chunk parity (staged by a prep wave), row = token, 16-byte
+    // vector u = value columns 8u..8u+7 of the workgroup's tile; the spare
+    // vector per row staggers the rows over the banks
+    static constexpr bool VST = NS != 4;
+    static constexpr int VU = 2 * NS;                 // 16-byte vectors per row
+    uint4 Vs[VST ? 2 : 1][VST ? C : 1][VU + 1];
 };
 
 // Prep waves per workgroup: six beside one or two scan waves, four beside
@@ -314,6 +325,35 @@ __global__ __launch_bounds__((NS + fast_prep_waves(NS)) * 64) void gdn_fwd_fast_
                     *reinterpret_cast<uint4*>(&s.K[kb3][r][8 * u]) = slice(stK[i]);
                     *reinterpret_cast<uint4*>(&s.Q[buf][r][8 * u]) = slice(stQ[i]);
                 }
+            });
+        };
+        // solve wave (one or two scan waves): the value tile of chunk cc (rows
+        // past the end of the sequence read as zero, and so does every row of
+        // a transition tile), loaded an iteration ahead and stored raw into
+        // LDS in phase A, where this wave is otherwise idle, so that the scan
+        // waves issue no global loads of their own (theirs would also wait for
+        // their earlier output stores: loads and stores share one counter)
+        constexpr int VU = L::VU;
+        constexpr int NVV = (C * VU + 63) / 64;
+        uint4 stV[NVV];
+        const buf_t vsbuf = buffer_over(vb, trans ? 0u : (uint32_t)T * dv * 2);
+        const uint32_t vcol = (uint32_t)((trans ? tile - p.n_tiles_v : tile) * DVT);
+        auto val_load = [&](int cc) __attribute__((always_inline)) {
+            const uint32_t t0 = (uint32_t)cc * C;
+            static_for<0, NVV>([&](auto I) {
+                constexpr int i = decltype(I)::value;
+                const int vi = lane + 64 * i;
+                if (i + 1 < NVV || vi < C * VU) {
+                    const uint32_t r = vi / VU, u = vi % VU;
+                    stV[i] = buf_load_16B(vsbuf, 2u * ((t0 + r) * dv + vcol + 8 * u));
+                }
+            });
+        };
+        auto val_store = [&](int cc) __attribute__((always_inline)) {
+            static_for<0, NVV>([&](auto I) {
+                constexpr int i = decltype(I)::value;
+                const int vi = lane + 64 * i;
+                if (i + 1 < NVV || vi < C * VU) s.Vs[cc & 1][vi / VU][vi % VU] = stV[i];
             });
         };
         // prep 0: gates of chunk cc (lane t holds token t of the chunk)
@@ -547,6 +587,13 @@ __global__ __launch_bounds__((NS + fast_prep_waves(NS)) * 64) void gdn_fwd_fast_
             constexpr bool stg = R::stager(w) >= 0;
             auto step = [&](auto PAR, int i) __attribute__((always_inline)) {
                 // ---- phase A ----
+                if constexpr (L::VST && w == R::solve_wave) {
+                    // the scan reads chunk i's values from the other buffer
+                    if (i + 1 >= 0 && i + 1 < nchunks) {
+                        val_store(i + 1);
+                        if (i + 2 < nchunks) val_load(i + 2);
+                    }
+                }
                 if constexpr (w == R::toff_wave) {
                     if (i >= 0) {
                         t_off(i);
@@ -579,6 +626,7 @@ __global__ __launch_bounds__((NS + fast_prep_waves(NS)) * 64) void gdn_fwd_fast_
                 __syncthreads();
             };
             if constexpr (w == R::vec_wave) gate_load(0);
+            if constexpr (L::VST && w == R::solve_wave) val_load(0);
             if constexpr (stg) kq_load(0);
             for (int i = -2; i < nchunks; i += 2) {
                 step(std::integral_constant<int, 0>{}, i);
@@ -596,12 +644,15 @@ __global__ __launch_bounds__((NS + fast_prep_waves(NS)) * 64) void gdn_fwd_fast_
     } else {
         // ============================== scan ===============================
         f32x4 Sacc[NK];            // Sacc[t][j] = S[col0 + n][16 t + 4 h + j]
-        // value rows of the next chunk, A operand of the transposing MFMA:
-        // lane (n, h) holds V[16 rt + n][col0 + 8 (h & 1) .. + 7] (lanes h >= 2
-        // repeat lanes h - 2; the selector gives them weight zero)
+        // value rows of a chunk, A operand of the transposing MFMA: lane
+        // (n, h) holds V[16 rt + n][col0 + 8 (h & 1) .. + 7] (lanes h >= 2
+        // repeat lanes h - 2; the selector gives them weight zero).  With
+        // one or two scan waves they are read from the tile a prep wave
+        // staged in LDS; with four (no prep wave to spare) each scan wave
+        // loads its own a chunk ahead, transition tiles from an empty buffer
+        // that reads zero.
         uint4 vraw[NT];
-        // (transition tiles: zero values, an empty buffer reads zero)
-        const buf_t vbuf = buffer_over(vb, trans ? 0u : (uint32_t)T * dv * 2);
+        const buf_t vbuf = buffer_over(vb, trans || L::VST ? 0u : (uint32_t)T * dv * 2);
         const uint32_t voff = 2u * (n * dv + col0 + 8 * (h & 1));
         auto v_load = [&](int cc) __attribute__((always_inline)) {
             const uint32_t t0 = (uint32_t)cc * C;
@@ -646,7 +697,7 @@ __global__ __launch_bounds__((NS + fast_prep_waves(NS)) * 64) void gdn_fwd_fast_
             for (int j = 0; j < 4; ++j)
                 Sacc[t][j] = trans ? (col0 + n == 16 * t + 4 * h + j ? 1.f : 0.f)
                              : (s0p && 16 * t < DKG) ? s0p[16 * t + 4 * h + j] : 0.f;
-        v_load(0);
+        if constexpr (!L::VST) v_load(0);
         // wait here for the initial state (and the first values): at the loop
         // head the state registers must not look like pending loads, or every
         // iteration would wait for all outstanding memory operations,
@@ -673,6 +724,15 @@ __global__ __launch_bounds__((NS + fast_prep_waves(NS)) * 64) void gdn_fwd_fast_
             }
         };
         kq_first(0);
+        // (one or two scan waves) a chunk's staged value rows, read at the end
+        // of the previous chunk like the first key and query slices (the
+        // solve wave stores them in the previous chunk's phase A)
+        auto v_first = [&](int cc) __attribute__((always_inline)) {
+            const uint4* vrow = &s.Vs[cc & 1][n][2 * wave + (h & 1)];
+#pragma unroll
+            for (int rt = 0; rt < NT; ++rt) vraw[rt] = vrow[16 * rt * (L::VU + 1)];
+        };
+        if constexpr (L::VST) v_first(0);
         // one chunk; PAR = parity of c (the LDS buffer of Q, T and P; keys by c mod 3)
         auto chunk = [&](auto PAR, int c) __attribute__((always_inline)) {
             constexpr int buf = decltype(PAR)::value;
@@ -708,10 +768,10 @@ __global__ __launch_bounds__((NS + fast_prep_waves(NS)) * 64) void gdn_fwd_fast_
 #pragma unroll
             for (int rt = 0; rt < NT; ++rt)
                 Vt[rt] = mfma_bf16(__builtin_bit_cast(bf16x8, vraw[rt]), vsel, zero4());
-            // the next chunk's values (past the last chunk every row lies
-            // outside the buffer and reads zero; loading unconditionally keeps
-            // the wait for them precise)
-            v_load(c + 1);
+            // (four scan waves) the next chunk's values; past the last chunk
+            // every row lies outside the buffer and reads zero, and loading
+            // unconditionally keeps the wait for them precise
+            if constexpr (!L::VST) v_load(c + 1);
             // Y = diag(beta) (V - diag(exp g) X)  (or eta V - beta exp(g) X)
             const float* f1b = ETA ? &s.eta[vb3][0] : &s.beta[vb3][0];
             const float* f2b = ETA ? &s.bge[vb3][0] : &s.eg[vb3][0];
@@ -816,7 +876,10 @@ __global__ __launch_bounds__((NS + fast_prep_waves(NS)) * 64) void gdn_fwd_fast_
                     Sacc[t] = mfma_h(ktop[t], vd[ss], Sacc[t]);
                     if (ss + 1 < NTS) ktop[t] = kt_one(ss + 1, t);
                 }
-            if (c + 1 < nchunks) kq_first(c + 1);
+            if (c + 1 < nchunks) {
+                kq_first(c + 1);
+                if constexpr (L::VST) v_first(c + 1);
+            }
             // O^T = diag(exp g) Z^T + V'^T P^T  (lane: row 16 rt + n, columns 4h..4h+3):
             // all products first, then the stores under one branch on the
             // output type; output rows past the end of the sequence fall
