@@ -127,6 +127,7 @@ WAVE_SHAPES = [
     (4, 16, 97, 64, 128, 32),     # two scan waves, d_k 64, 32-token chunks
     (8, 32, 150, 64, 64, 64),     # four scan waves
     (16, 16, 97, 128, 128, 32),   # four scan waves, 32-token chunks
+    (8, 32, 100, 64, 256, 64),    # four scan waves, d_v 256 (non-temporal fp32 stores)
 ]
 
 
