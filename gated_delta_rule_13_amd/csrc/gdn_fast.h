@@ -141,11 +141,13 @@ struct alignas(16) FastLds {
     _Float16 Q[2][C][KP];
     // with one or two scan waves, the values of the scan's chunks as raw
     // bf16 by chunk parity (staged by a prep wave), row = token, 16-byte
-    // vector u = value columns 8u..8u+7 of the workgroup's tile; the spare
-    // vector per row staggers the rows over the banks
+    // vector u = value columns 8u..8u+7 of the workgroup's tile.  Row stride
+    // VS = 2 x odd vectors: a scan wave's 16-byte reads of eight rows by two
+    // halves then fall on 16 distinct 16-byte bank groups.
     static constexpr bool VST = NS != 4;
     static constexpr int VU = 2 * NS;                 // 16-byte vectors per row
-    uint4 Vs[VST ? 2 : 1][VST ? C : 1][VU + 1];
+    static constexpr int VS = NS == 1 ? 2 : 6;        // row stride (16-byte vectors)
+    uint4 Vs[VST ? 2 : 1][VST ? C : 1][VS];
 };
 
 // Prep waves per workgroup: six beside one or two scan waves, four beside
@@ -232,6 +234,7 @@ __global__ __launch_bounds__((NS + fast_prep_waves(NS)) * 64) void gdn_fwd_fast_
     constexpr int BP_ = L::BP;
     static_assert(DK % 32 == 0 && C % 16 == 0, "shape");
     static_assert(sizeof(L) <= 160 * 1024, "LDS budget");
+    static_assert(!L::VST || L::VU <= L::VS, "value tile row");
     __shared__ L s;
 
     const int tid = threadIdx.x;
@@ -730,7 +733,7 @@ __global__ __launch_bounds__((NS + fast_prep_waves(NS)) * 64) void gdn_fwd_fast_
         auto v_first = [&](int cc) __attribute__((always_inline)) {
             const uint4* vrow = &s.Vs[cc & 1][n][2 * wave + (h & 1)];
 #pragma unroll
-            for (int rt = 0; rt < NT; ++rt) vraw[rt] = vrow[16 * rt * (L::VU + 1)];
+            for (int rt = 0; rt < NT; ++rt) vraw[rt] = vrow[16 * rt * L::VS];
         };
         if constexpr (L::VST) v_first(0);
         // one chunk; PAR = parity of c (the LDS buffer of Q, T and P; keys by c mod 3)
