@@ -119,22 +119,23 @@ int device_cus() {
 }
 
 // Scan waves per workgroup of the pipelined kernels (16 value columns each,
-// one workgroup per compute unit): the choice of 1, 2 or 4 (dividing
-// d_v / 16) that needs the fewest rounds of workgroups over the compute
-// units, a four-wave workgroup weighing 1.4 rounds (its prep waves serve
-// four slices; measured at d_k 96, d_v 192: 160 us for one round of them
-// against about 110 us per round of two-wave workgroups); ties go to the
-// smaller workgroup.
-int choose_scan_waves(const gdn_shape& s) {
+// one workgroup per compute unit): the choice among 1, 2, 4 and, for the
+// fused kernel, 3 (dividing d_v / 16) that needs the fewest rounds of
+// workgroups over the compute units, a four-wave workgroup weighing 1.4
+// rounds (its four prep waves serve four slices; measured at d_k 96,
+// d_v 192: 160 us for one round of them against about 110 us per round of
+// two-wave workgroups) and a three-wave one 1.2 (five prep waves; 141 us
+// for one round at that shape); ties go to the smaller workgroup.
+int choose_scan_waves(const gdn_shape& s, bool three = false) {
     const long heads = (long)s.B * s.H;
     const int cols16 = s.d_v / 16;
     const long cus = device_cus();
     int best = 1;
     double best_cost = 1e300;
-    for (int ns : {1, 2, 4}) {
-        if (cols16 % ns != 0) continue;
+    for (int ns : {1, 2, 3, 4}) {
+        if (cols16 % ns != 0 || (ns == 3 && !three)) continue;
         const long wgs = heads * (cols16 / ns);
-        const double cost = (double)((wgs + cus - 1) / cus) * (ns == 4 ? 1.4 : 1.0);
+        const double cost = (double)((wgs + cus - 1) / cus) * (ns == 4 ? 1.4 : ns == 3 ? 1.2 : 1.0);
         if (cost < best_cost) {
             best = ns;
             best_cost = cost;
@@ -151,7 +152,7 @@ int choose_scan_waves(const gdn_shape& s) {
 // segments and corrects the later segments' outputs (gdn_seq.h).
 // Cost model in microseconds, fitted to measurements on MI355X (one fused
 // kernel iteration: 1.4 us at d_k <= 64, 1.6 us above, times 1.25 for two
-// scan waves and 1.75 for four):
+// scan waves, 1.5 for three and 1.75 for four):
 //   plain  rounds(B H d_v / (16 ns)) (n_chunks + 2) it
 //   seq    rounds(B H (n_v + (n_seg - 1) (n_v + n_k))) (L + 2) it
 //          + 6.5 (the second launch and its first memory round trip)
@@ -169,7 +170,7 @@ struct Plan {
 };
 
 double iter_us(int dk, int ns) {
-    return (dk <= 64 ? 1.4 : 1.6) * (ns == 1 ? 1.0 : ns == 2 ? 1.25 : 1.75);
+    return (dk <= 64 ? 1.4 : 1.6) * (ns == 1 ? 1.0 : ns == 2 ? 1.25 : ns == 3 ? 1.5 : 1.75);
 }
 long rounds_over_cus(long wgs) {
     const long cus = device_cus();
@@ -214,7 +215,7 @@ void plan_workspace(const gdn_shape& s, Plan* pl) {
 // plan stays inside that range.
 Plan make_plan(const gdn_shape& s, int seg_chunks) {
     Plan pl;
-    pl.ns = choose_scan_waves(s);
+    pl.ns = choose_scan_waves(s, true);
     pl.seg_len = s.T;
     const long nchunks = (s.T + s.chunk_size - 1) / s.chunk_size;
     int best_L = 0;
@@ -320,7 +321,7 @@ gdn_status run_chunk(const gdn_shape* s_in, const ChunkArgs& a, Path path, void*
     const bool bf = s->qkv_dtype == GDN_BF16;
     const bool fused = bf && path == Path::kFast && fast_pair(s->chunk_size, s->d_k);
     Plan plan;
-    plan.ns = choose_scan_waves(*s);
+    plan.ns = choose_scan_waves(*s, true);
     if (fused && seg_chunks >= 0) plan = make_plan(*s, seg_chunks);
     if (seg_chunks > 0 && !fused &&
         (long)seg_chunks * s->chunk_size < (long)s->T)

@@ -26,17 +26,17 @@
 //
 // Work is split by role inside the workgroup.  NS "scan" waves own 16 value
 // columns each and that slice of the fp32 state (S^T in MFMA accumulators);
-// six "prep" waves beside one or two scan waves, four beside four (the
-// roles below are spread over them by FastRoles), build chunk-local
-// matrices one or two chunks ahead.  Iteration i (chunk i on the scan
-// waves) has two phases separated by workgroup barriers:
+// six "prep" waves beside one or two scan waves, five beside three, four
+// beside four (the roles below are spread over them by FastRoles), build
+// chunk-local matrices one or two chunks ahead.  Iteration i (chunk i on
+// the scan waves) has two phases separated by workgroup barriers:
 //   phase A  scan     X_i = K_i S^T, Z^T_i = S Q_i^T
 //            T blocks blocks of T_i below the diagonal (T_bb of chunk i and
 //                     its A blocks are from iteration i - 1)
 //            strips   row strips of chunk i + 1: Gram and score tiles formed
 //                     into the diagonal blocks of A (fp32), the blocks below
 //                     them (fp16) and the masked decayed scores P (fp16)
-//            values   (one or two scan waves) the values of chunk i + 1
+//            values   (up to three scan waves) the values of chunk i + 1
 //                     into LDS, on the solve wave
 //   phase B  scan     Y, V' = T_i Y, state update, O = diag(exp g) Z + P V'
 //            vectors  decay vectors of chunk i + 2
@@ -139,7 +139,7 @@ struct alignas(16) FastLds {
     // h = 0..3), so an MFMA operand slice is one aligned 16-byte read
     _Float16 K[3][C][KP];
     _Float16 Q[2][C][KP];
-    // with one or two scan waves, the values of the scan's chunks as raw
+    // with up to three scan waves, the values of the scan's chunks as raw
     // bf16 by chunk parity (staged by a prep wave), row = token, 16-byte
     // vector u = value columns 8u..8u+7 of the workgroup's tile.  Row stride
     // VS = 2 x odd vectors: a scan wave's 16-byte reads of eight rows by two
@@ -150,17 +150,20 @@ struct alignas(16) FastLds {
     uint4 Vs[VST ? 2 : 1][VST ? C : 1][VS];
 };
 
-// Prep waves per workgroup: six beside one or two scan waves, four beside
-// four (eight waves in all at most, two per SIMD).
-constexpr int fast_prep_waves(int ns) { return ns == 4 ? 4 : 6; }
+// Prep waves per workgroup: six beside one or two scan waves, five beside
+// three, four beside four (eight waves in all at most, two per SIMD).
+constexpr int fast_prep_waves(int ns) { return ns == 4 ? 4 : ns == 3 ? 5 : 6; }
 
 // Roles of the prep waves.  The waves of a workgroup are spread over the
 // four SIMDs of the compute unit so that waves w and w + 4 share one; the
-// roles are placed so that the two prep waves beside the scan waves (prep
-// waves 2 and 3 when there are six) carry the latency-bound, issue-light
-// jobs (the blocks of T below the diagonal, the decay vectors, the diagonal
-// solves) and the issue-heavy ones (Gram strips, staging) sit together on
-// the other two SIMDs.
+// roles are placed so that the prep waves beside the scan waves (prep waves
+// 2 and 3 when there are six, 1, 2 and 3 when there are five) carry the
+// latency-bound, issue-light jobs (the blocks of T below the diagonal, the
+// decay vectors, the diagonal solves, the value staging) and the
+// issue-heavy ones (Gram strips, staging) sit together on the other SIMDs.
+// With five, the SIMD that has no scan wave carries two strip waves of 24
+// tile products each, and the prep waves beside scan waves 1 and 2 one of
+// 16 each.
 //   strips: row strip rt holds the tiles (rt, ct), ct = 0..rt, of both A and
 //           the scores P;
 //   stagers: convert and store the keys and queries of a chunk.
@@ -168,11 +171,12 @@ template <int NS, int NT>
 struct FastRoles {
     static constexpr int NP = fast_prep_waves(NS);
     static constexpr int NSTG = NP == 6 ? 4 : 3;
-    static constexpr int toff_wave = NP == 6 ? 2 : 0;
-    static constexpr int vec_wave = NP == 6 ? 2 : 0;
-    static constexpr int solve_wave = NP == 6 ? 3 : 0;
+    static constexpr int toff_wave = NP == 6 ? 2 : NP == 5 ? 1 : 0;
+    static constexpr int vec_wave = NP == 6 ? 2 : NP == 5 ? 1 : 0;
+    static constexpr int solve_wave = NP == 6 ? 3 : NP == 5 ? 2 : 0;
     static constexpr int stager(int pw) {
         if (NP == 6) return pw == 0 ? 0 : pw == 1 ? 1 : pw == 4 ? 2 : pw == 5 ? 3 : -1;
+        if (NP == 5) return pw == 0 ? 0 : pw == 3 ? 1 : pw == 4 ? 2 : -1;
         return pw >= 1 ? pw - 1 : -1;
     }
     // Gram segments: (row strip rt, tile columns c0 <= ct < c1), encoded
@@ -192,6 +196,21 @@ struct FastRoles {
             if (NT == 2) {
                 if (w == 0) return j == 0 ? seg_code(1, 0, 2) : -1;
                 if (w == 1) return j == 0 ? seg_code(0, 0, 1) : -1;
+                return -1;
+            }
+            return (w == 0 && j == 0) ? seg_code(0, 0, 1) : -1;
+        }
+        if (NP == 5) {
+            if (NT == 4) {
+                if (w == 0) return j == 0 ? seg_code(3, 0, 2) : j == 1 ? seg_code(0, 0, 1) : -1;
+                if (w == 2) return j == 0 ? seg_code(1, 0, 2) : -1;
+                if (w == 3) return j == 0 ? seg_code(3, 2, 4) : -1;
+                if (w == 4) return j == 0 ? seg_code(2, 0, 3) : -1;
+                return -1;
+            }
+            if (NT == 2) {
+                if (w == 0) return j == 0 ? seg_code(1, 0, 2) : -1;
+                if (w == 4) return j == 0 ? seg_code(0, 0, 1) : -1;
                 return -1;
             }
             return (w == 0 && j == 0) ? seg_code(0, 0, 1) : -1;
@@ -330,7 +349,7 @@ __global__ __launch_bounds__((NS + fast_prep_waves(NS)) * 64) void gdn_fwd_fast_
                 }
             });
         };
-        // solve wave (one or two scan waves): the value tile of chunk cc (rows
+        // solve wave (up to three scan waves): the value tile of chunk cc (rows
         // past the end of the sequence read as zero, and so does every row of
         // a transition tile), loaded an iteration ahead and stored raw into
         // LDS in phase A, where this wave is otherwise idle, so that the scan
@@ -650,7 +669,7 @@ __global__ __launch_bounds__((NS + fast_prep_waves(NS)) * 64) void gdn_fwd_fast_
         // value rows of a chunk, A operand of the transposing MFMA: lane
         // (n, h) holds V[16 rt + n][col0 + 8 (h & 1) .. + 7] (lanes h >= 2
         // repeat lanes h - 2; the selector gives them weight zero).  With
-        // one or two scan waves they are read from the tile a prep wave
+        // up to three scan waves they are read from the tile a prep wave
         // staged in LDS; with four (no prep wave to spare) each scan wave
         // loads its own a chunk ahead, transition tiles from an empty buffer
         // that reads zero.
@@ -727,7 +746,7 @@ __global__ __launch_bounds__((NS + fast_prep_waves(NS)) * 64) void gdn_fwd_fast_
             }
         };
         kq_first(0);
-        // (one or two scan waves) a chunk's staged value rows, read at the end
+        // (up to three scan waves) a chunk's staged value rows, read at the end
         // of the previous chunk like the first key and query slices (the
         // solve wave stores them in the previous chunk's phase A)
         auto v_first = [&](int cc) __attribute__((always_inline)) {

@@ -35,6 +35,7 @@ FwdLauncher GDN_NAME(GDN_C, GDN_DK)(int ns, bool eta, bool seg) {
     switch (ns) {
         case 1: return eta ? launch<1, true, false> : launch<1, false, false>;
         case 2: return eta ? launch<2, true, false> : launch<2, false, false>;
+        case 3: return eta ? launch<3, true, false> : launch<3, false, false>;
         case 4: return eta ? launch<4, true, false> : launch<4, false, false>;
     }
     return nullptr;

@@ -16,7 +16,7 @@ using RecLauncher = void (*)(const RecParams&, long nblocks, hipStream_t);
 using SeqLauncher = void (*)(const SeqParams&, hipStream_t);
 
 // fp16-operand fused kernel (bf16 inputs): C in {16, 32, 64}, d_k in
-// {16, 32, 64, 96, 128} (and 256 with C <= 32), ns scan waves in {1, 2, 4};
+// {16, 32, 64, 96, 128} (and 256 with C <= 32), ns scan waves in {1, 2, 3, 4};
 // seg: the sequence-parallel launch (ns = 1 only).  Null when the shape is
 // not built.  One definition per (C, d_k), in the object built from
 // gdn_inst_fast.hip with that pair.

@@ -116,11 +116,12 @@ F32_SHAPES = [
 ]
 
 
-# Head counts large enough that the kernel runs two or four scan waves per
-# workgroup (the launch picks four when B*H*d_v/64 >= 256, else two when
-# B*H*d_v/32 >= 256); with one or two the values are staged through LDS by a
-# prep wave, with four the scan waves load them.  Ragged T in every case;
-# every head is compared.
+# Head counts large enough that the kernel runs two, three or four scan
+# waves per workgroup (the launch weighs a round of four-wave workgroups as
+# 1.4 rounds and of three-wave ones as 1.2, three needing d_v / 16 divisible
+# by 3); with up to three the values are staged through LDS by a prep wave,
+# with four the scan waves load them.  Ragged T in every case; every head is
+# compared.
 WAVE_SHAPES = [
     # (B, H, T, dk, dv, C)
     (4, 16, 333, 128, 128, 64),   # two scan waves
@@ -128,6 +129,9 @@ WAVE_SHAPES = [
     (8, 32, 150, 64, 64, 64),     # four scan waves
     (16, 16, 97, 128, 128, 32),   # four scan waves, 32-token chunks
     (8, 32, 100, 64, 256, 64),    # four scan waves, d_v 256 (non-temporal fp32 stores)
+    (2, 30, 300, 96, 192, 64),    # three scan waves (five prep waves), the Olmo head shape
+    (6, 16, 150, 128, 96, 32),    # three scan waves, 32-token chunks
+    (8, 16, 77, 64, 48, 16),      # three scan waves, 16-token chunks
 ]
 
 
