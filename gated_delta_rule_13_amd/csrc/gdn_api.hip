@@ -394,11 +394,12 @@ gdn_status run_chunk(const gdn_shape* s_in, const ChunkArgs& a, Path path, void*
     const long grid_units = pipelined ? (units + 7) / 8 * 8 : units;
     // fp32 output written through at system scope keeps the written bytes at
     // the output size.  Where the scan waves load their own values (the
-    // split-bf16 kernel; the fused kernel with four scan waves) their waits
-    // for those loads also wait for their earlier stores, and at d_v >= 256
-    // plain non-temporal stores measured 6 % faster there (the write-back of
-    // partly written lines costs bytes, not time).
-    p.o_wt = s->d_v < 256 || (fused && nw != 4);
+    // split-bf16 kernel; the fused kernel with four scan waves and four prep
+    // waves) their waits for those loads also wait for their earlier stores,
+    // and at d_v >= 256 plain non-temporal stores measured 6 % faster there
+    // (the write-back of partly written lines costs bytes, not time).
+    const bool staged = fused && gdn::fast_prep_waves(nw, s->chunk_size, s->d_k < 32 ? 32 : s->d_k) != 4;
+    p.o_wt = s->d_v < 256 || staged;
     const long nblocks = grid_units * p.n_tiles;
     if (nblocks > 0x7fffffffL) return fail(GDN_ERR_BAD_SHAPE, "grid too large");
     if (finish) {

@@ -144,15 +144,12 @@ struct alignas(16) FastLds {
     // vector u = value columns 8u..8u+7 of the workgroup's tile.  Row stride
     // VS = 2 x odd vectors: a scan wave's 16-byte reads of eight rows by two
     // halves then fall on 16 distinct 16-byte bank groups.
-    static constexpr bool VST = NS != 4;
+    static constexpr bool VST = fast_prep_waves(NS, C, DK) != 4;
     static constexpr int VU = 2 * NS;                 // 16-byte vectors per row
-    static constexpr int VS = NS == 1 ? 2 : 6;        // row stride (16-byte vectors)
+    static constexpr int VS = NS == 1 ? 2 : NS == 4 ? 10 : 6;   // row stride (16-byte vectors)
     uint4 Vs[VST ? 2 : 1][VST ? C : 1][VS];
 };
 
-// Prep waves per workgroup: six beside one or two scan waves, five beside
-// three, four beside four (eight waves in all at most, two per SIMD).
-constexpr int fast_prep_waves(int ns) { return ns == 4 ? 4 : ns == 3 ? 5 : 6; }
 
 // Roles of the prep waves.  The waves of a workgroup are spread over the
 // four SIMDs of the compute unit so that waves w and w + 4 share one; the
@@ -167,14 +164,21 @@ constexpr int fast_prep_waves(int ns) { return ns == 4 ? 4 : ns == 3 ? 5 : 6; }
 //   strips: row strip rt holds the tiles (rt, ct), ct = 0..rt, of both A and
 //           the scores P;
 //   stagers: convert and store the keys and queries of a chunk.
-template <int NS, int NT>
+template <int NS, int NT, int DK>
 struct FastRoles {
-    static constexpr int NP = fast_prep_waves(NS);
+    static constexpr int NP = fast_prep_waves(NS, 16 * NT, DK);
+    // six prep waves beside four scan waves: every SIMD holds a scan wave;
+    // prep waves 0 to 3 (one per SIMD) stage the keys and queries, 2 and 3
+    // also form the Gram strips, and 4 and 5 (on the SIMDs of scan waves 0
+    // and 1) carry the blocks of T with the decay vectors, and the diagonal
+    // solves with the value staging
+    static constexpr bool WIDE = NP == 6 && NS == 4;
     static constexpr int NSTG = NP == 6 ? 4 : 3;
-    static constexpr int toff_wave = NP == 6 ? 2 : NP == 5 ? 1 : 0;
-    static constexpr int vec_wave = NP == 6 ? 2 : NP == 5 ? 1 : 0;
-    static constexpr int solve_wave = NP == 6 ? 3 : NP == 5 ? 2 : 0;
+    static constexpr int toff_wave = WIDE ? 4 : NP == 6 ? 2 : NP == 5 ? 1 : 0;
+    static constexpr int vec_wave = WIDE ? 4 : NP == 6 ? 2 : NP == 5 ? 1 : 0;
+    static constexpr int solve_wave = WIDE ? 5 : NP == 6 ? 3 : NP == 5 ? 2 : 0;
     static constexpr int stager(int pw) {
+        if (WIDE) return pw < 4 ? pw : -1;
         if (NP == 6) return pw == 0 ? 0 : pw == 1 ? 1 : pw == 4 ? 2 : pw == 5 ? 3 : -1;
         if (NP == 5) return pw == 0 ? 0 : pw == 3 ? 1 : pw == 4 ? 2 : -1;
         return pw >= 1 ? pw - 1 : -1;
@@ -185,6 +189,14 @@ struct FastRoles {
     // that the two SIMDs of the issue-heavy waves carry 40 each.
     static constexpr int seg_code(int rt, int c0, int c1) { return (rt << 16) | (c0 << 8) | c1; }
     static constexpr int seg(int w, int j) {
+        if (WIDE) {   // (chunks of at most 32 tokens)
+            if (NT == 2) {
+                if (w == 2) return j == 0 ? seg_code(1, 0, 2) : -1;
+                if (w == 3) return j == 0 ? seg_code(0, 0, 1) : -1;
+                return -1;
+            }
+            return (w == 2 && j == 0) ? seg_code(0, 0, 1) : -1;
+        }
         if (NP == 6) {
             if (NT == 4) {
                 if (w == 0) return j == 0 ? seg_code(3, 0, 2) : j == 1 ? seg_code(0, 0, 1) : -1;
@@ -238,8 +250,8 @@ struct FastRoles {
 // keys and queries are padded with zeros as they are staged and the state's
 // extra rows stay zero, so the products are those of d_k = DKG.
 template <int C, int DK, int NS, bool ETA, bool SEG, int DKG = DK>
-__global__ __launch_bounds__((NS + fast_prep_waves(NS)) * 64) void gdn_fwd_fast_kernel(FwdParams p) {
-    using R = FastRoles<NS, C / 16>;
+__global__ __launch_bounds__((NS + fast_prep_waves(NS, C, DK)) * 64) void gdn_fwd_fast_kernel(FwdParams p) {
+    using R = FastRoles<NS, C / 16, DK>;
     constexpr int NP = R::NP;
     using L = FastLds<C, DK, NS, ETA>;
     constexpr int NT = C / 16;
@@ -254,6 +266,7 @@ __global__ __launch_bounds__((NS + fast_prep_waves(NS)) * 64) void gdn_fwd_fast_
     static_assert(DK % 32 == 0 && C % 16 == 0, "shape");
     static_assert(sizeof(L) <= 160 * 1024, "LDS budget");
     static_assert(!L::VST || L::VU <= L::VS, "value tile row");
+    static_assert(!R::WIDE || NT <= 2, "six prep waves beside four scan waves: chunks of at most 32");
     __shared__ L s;
 
     const int tid = threadIdx.x;

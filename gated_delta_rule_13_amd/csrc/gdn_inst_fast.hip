@@ -21,7 +21,7 @@ namespace {
 template <int NS, bool ETA, bool SEG>
 void launch(const FwdParams& p, long nblocks, hipStream_t st) {
     hipLaunchKernelGGL((gdn_fwd_fast_kernel<GDN_C, GDN_DKK, NS, ETA, SEG, GDN_DK>), dim3((unsigned)nblocks),
-                       dim3((NS + fast_prep_waves(NS)) * 64), 0, st, p);
+                       dim3((NS + fast_prep_waves(NS, GDN_C, GDN_DKK)) * 64), 0, st, p);
 }
 }  // namespace
 

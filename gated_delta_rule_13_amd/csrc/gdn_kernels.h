@@ -27,6 +27,15 @@
 
 namespace gdn {
 
+// Prep waves per workgroup of the fp16-operand fused kernel (gdn_fast.h):
+// six beside one or two scan waves, five beside three, and beside four six
+// at chunks of up to 32 tokens with d_k up to 128 (ten waves, whose
+// registers still fit three waves on a SIMD), else four (eight waves in
+// all, two per SIMD).
+constexpr int fast_prep_waves(int ns, int C, int dk) {
+    return ns == 3 ? 5 : (ns == 4 && (C > 32 || dk > 128)) ? 4 : 6;
+}
+
 struct FwdParams {
     const void* q;
     const void* k;
