@@ -122,27 +122,24 @@ def test_null_eta_is_the_plain_entry():
         assert rel_err(S_.cpu().numpy(), Sr) < TOL["bf16"]
 
 
-def test_random_eta_two_scan_waves_ragged():
-    """Random eta on a head count that runs two scan waves (values staged in
-    LDS), ragged T, sampled heads against the oracle."""
-    x = make_random(4, 16, 200, 128, 128, seed=23, s0_std=0.05)
-    g = torch.Generator().manual_seed(23)
+@pytest.mark.parametrize("B,H,T,dk,dv,C,waves", [
+    (4, 16, 200, 128, 128, 64, "two scan waves"),
+    (2, 30, 150, 96, 192, 64, "three scan waves"),
+    (16, 16, 97, 128, 128, 32, "four scan waves, six prep waves"),
+    (8, 32, 70, 64, 64, 64, "four scan waves, four prep waves"),
+])
+def test_random_eta_scan_wave_counts_ragged(B, H, T, dk, dv, C, waves):
+    """Random eta on head counts that run two, three or four scan waves per
+    workgroup, ragged T, every head against the oracle."""
+    x = make_random(B, H, T, dk, dv, chunk=C, seed=23 + T, s0_std=0.05)
+    g = torch.Generator().manual_seed(23 + T)
     eta = 1.5 * torch.rand(x["beta"].shape, generator=g)
-    say("case: random eta, B4 H16 T200 d128 (two scan waves, sampled heads)")
+    say(f"case: random eta, B{B} H{H} T{T} dk{dk} dv{dv} C{C} ({waves}, all heads)")
     d = to_dev(x)
     O, S = gdn.gdn_chunk_fwd_eta(d["q"], d["k"], d["v"], d["alpha"], d["beta"], eta.cuda(),
-                                 d["S0"], chunk_size=64)
+                                 d["S0"], chunk_size=C)
     torch.cuda.synchronize()
-    heads = [(0, 0), (2, 5), (3, 15)]
-    Os, Ss = [], []
-    for b, h in heads:
-        pick = lambda t: None if t is None else t[b:b + 1, h:h + 1]
-        Or, Sr = oracle.recurrent(pick(x["q"]), pick(x["k"]), pick(x["v"]), pick(x["alpha"]),
-                                  pick(x["beta"]), S0=pick(x["S0"]), eta=pick(eta))
-        Os.append(Or[0, 0])
-        Ss.append(Sr[0, 0])
-    Og = np.stack([O[b, h].cpu().numpy() for b, h in heads])
-    Sg = np.stack([S[b, h].cpu().numpy() for b, h in heads])
-    eo, es = rel_err(Og, np.stack(Os)), rel_err(Sg, np.stack(Ss))
+    Or, Sr = oracle.recurrent(x["q"], x["k"], x["v"], x["alpha"], x["beta"], S0=x["S0"], eta=eta)
+    eo, es = rel_err(O.cpu().numpy(), Or), rel_err(S.cpu().numpy(), Sr)
     say(f"  O {eo:.3e}  S {es:.3e}")
     assert eo < TOL["bf16"] and es < TOL["bf16"]
