@@ -23,8 +23,8 @@ from tests.gpu_helpers import TOL, elem_err, nan_outputs, rel_err, say, to_dev
 pytestmark = pytest.mark.gpu
 
 # (B, H, T, d_k, d_v, C, gate scales per chunk, with eta)
-# scan waves per workgroup follow from B*H*d_v (see test_parity_gpu):
-# B*H*d_v/16 < 512 -> one, >= 512 -> two, >= 1024 -> four
+# scan waves per workgroup follow from the launch's rounds of workgroups
+# (see test_parity_gpu); four scan waves at C = 32 run beside six prep waves
 CASES = [
     (1, 2, 333, 128, 128, 64, (4.0,), False),            # one scan wave, all strong
     (1, 2, 333, 128, 128, 64, (0.05, 4.0), False),       # alternating weak / strong
@@ -35,6 +35,8 @@ CASES = [
     (8, 16, 150, 128, 128, 64, (4.0, 0.05), False),      # four scan waves
     (16, 16, 97, 128, 128, 32, (8.0, 0.05), True),       # four scan waves, C = 32, eta
     (8, 32, 130, 64, 64, 64, (0.05, 4.0), False),        # four scan waves, d_k 64
+    (2, 30, 150, 96, 192, 64, (0.05, 4.0), False),       # three scan waves
+    (2, 30, 97, 96, 192, 64, (4.0,), True),              # three scan waves, eta
 ]
 
 
