@@ -132,6 +132,8 @@ WAVE_SHAPES = [
     (2, 30, 300, 96, 192, 64),    # three scan waves (five prep waves), the Olmo head shape
     (6, 16, 150, 128, 96, 32),    # three scan waves, 32-token chunks
     (8, 16, 77, 64, 48, 16),      # three scan waves, 16-token chunks
+    (16, 16, 77, 64, 64, 16),     # four scan waves beside six prep waves, 16-token chunks
+    (8, 32, 70, 256, 64, 32),     # four scan waves beside four prep waves at d_k 256
 ]
 
 
