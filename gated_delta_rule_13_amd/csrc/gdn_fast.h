@@ -321,9 +321,9 @@ __global__ __launch_bounds__((NS + fast_prep_waves(NS, C, DK)) * 64) void gdn_fw
         // raw bf16 key / query tiles of the next chunk to stage: loaded an
         // iteration ahead, converted into LDS, then reloaded with the next
         uint4 stK[NKV], stQ[NKV];
-        float stA = 1.f, stB = 0.f, stE = 0.f;  // prep 0: gates of the next chunk to prepare
+        float stA = 1.f, stB = 0.f, stE = 0.f;  // vector wave: gates of the next chunk to prepare
 
-        // prep 1+: global loads of chunk cc's keys and queries (rows past the
+        // stagers: global loads of chunk cc's keys and queries (rows past the
         // end of the sequence read as zero).  Staging vector vi is the 16-byte
         // k-order slice u = vi % (DK / 8) of row vi / (DK / 8): d_k
         // 32 (u / 4) + 4 (u % 4) .. + 3 and the four 16 further on, fetched as
@@ -345,7 +345,7 @@ __global__ __launch_bounds__((NS + fast_prep_waves(NS, C, DK)) * 64) void gdn_fw
                 }
             });
         };
-        // prep 1+: chunk cc's keys and queries into LDS as fp16, one k-order
+        // stagers: chunk cc's keys and queries into LDS as fp16, one k-order
         // slice per staging vector
         auto kq_store = [&](int cc) __attribute__((always_inline)) {
             const int buf = cc & 1, kb3 = mod3(cc);
@@ -391,7 +391,7 @@ __global__ __launch_bounds__((NS + fast_prep_waves(NS, C, DK)) * 64) void gdn_fw
                 if (i + 1 < NVV || vi < C * VU) s.Vs[cc & 1][vi / VU][vi % VU] = stV[i];
             });
         };
-        // prep 0: gates of chunk cc (lane t holds token t of the chunk)
+        // vector wave: gates of chunk cc (lane t holds token t of the chunk)
         auto gate_load = [&](int cc) __attribute__((always_inline)) {
             const int t0 = cc * C, Lc = min(C, T - t0);
             const int tt = t0 + min(lane, Lc - 1);
@@ -399,7 +399,7 @@ __global__ __launch_bounds__((NS + fast_prep_waves(NS, C, DK)) * 64) void gdn_fw
             stB = bb[tt];
             if constexpr (ETA) stE = eb[tt];
         };
-        // prep 0: decay vectors of chunk cc into vector buffer mod3(cc);
+        // vector wave: decay vectors of chunk cc into vector buffer mod3(cc);
         // padding tokens are identity transitions (alpha = 1, beta = eta = 0)
         auto vectors = [&](int cc) __attribute__((always_inline)) {
             const int vb3 = mod3(cc);
@@ -504,7 +504,7 @@ __global__ __launch_bounds__((NS + fast_prep_waves(NS, C, DK)) * 64) void gdn_fw
                 });
             });
         };
-        // prep 0: T_bb = (I - A_bb)^{-1} for all diagonal blocks of chunk cc:
+        // solve wave: T_bb = (I - A_bb)^{-1} for all diagonal blocks of chunk cc:
         // lane (b, i) computes row i of T_bb from T = I + T A by substitution
         // from the last column down,  T[i][k] = [i == k] + sum_{m > k} T[i][m] A[m][k],
         // adding each final T[i][m] into every earlier column's partial sum.
@@ -544,7 +544,7 @@ __global__ __launch_bounds__((NS + fast_prep_waves(NS, C, DK)) * 64) void gdn_fw
                         to_h4(f32x4{x[4 * q], x[4 * q + 1], x[4 * q + 2], x[4 * q + 3]});
             }
         };
-        // prep 0: the blocks of T below the diagonal of chunk cc, by distance
+        // T-blocks wave: the blocks of T below the diagonal of chunk cc, by distance
         // from the diagonal:  T_bc = T_bb R,  R = sum_{c<=k<b} A_bk T_kc.
         // Lane (n, h) holds T_bc[4h + j][n] (accumulator layout), which is
         // also the B-operand layout of the next products.
