@@ -54,6 +54,9 @@ STAGE_TOL = 4e-3
     (1, 1, 70, 64, 32, 32),
     (1, 2, 45, 64, 48, 16),
     (4, 16, 130, 128, 128, 64),  # two scan waves per workgroup
+    (2, 30, 130, 96, 192, 64),   # three scan waves, five prep waves
+    (16, 16, 64, 128, 128, 32),  # four scan waves, six prep waves
+    (8, 32, 100, 64, 64, 64),    # four scan waves, four prep waves
     (1, 2, 100, 16, 32, 32),     # d_k 16, zero-padded
 ])
 def test_stages_match_chunk_matrices(B, H, T, dk, dv, C):
